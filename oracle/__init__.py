@@ -1,0 +1,132 @@
+"""CPU fp64 oracle for causal prefill attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU product path
+(``causal_prefill_attention_attn_amd``) never imports it and shares no code
+with it.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, binary64, OpenMP over
+query rows); this module only builds that file with gcc and marshals numpy
+arrays through ctypes.  See the header of ``attn_oracle.c`` for the
+definition it computes and the passages of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "libattn_oracle.so")
+
+BF16 = 0
+FP8 = 1
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile attn_oracle.c with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_bf16_decode.restype = ctypes.c_double
+        lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_descale_amax.restype = ctypes.c_float
+        lib.oracle_descale_amax.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+        lib.oracle_quantize_e4m3.restype = None
+        lib.oracle_quantize_e4m3.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                             ctypes.c_void_p]
+        lib.oracle_attn.restype = ctypes.c_int
+        lib.oracle_attn.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_float, ctypes.c_float, ctypes.c_float,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.oracle_bf16_decode(int(b)) for b in flat], np.float64).reshape(np.shape(bits))
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    lib = _load()
+    table = np.array([lib.oracle_e4m3_decode(c) for c in range(256)], np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def encode_e4m3_scalar(x: float) -> int:
+    return int(_load().oracle_e4m3_encode(float(np.float32(x))))
+
+
+def descale_amax(x: np.ndarray) -> float:
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    return float(_load().oracle_descale_amax(_ptr(a), a.size))
+
+
+def quantize_e4m3(x: np.ndarray, descale: float) -> np.ndarray:
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(a.shape, np.uint8)
+    _load().oracle_quantize_e4m3(_ptr(a), a.size, ctypes.c_float(descale), _ptr(out))
+    return out
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: int, tau: float,
+              causal: bool = True, rows=None, q_descale: float = 1.0, k_descale: float = 1.0,
+              v_descale: float = 1.0):
+    """fp64 attention on raw element encodings.
+
+    q, k: [B,S,H,d_qk]; v: [B,S,H,d_v]; uint16 bf16 bit patterns (dtype BF16)
+    or uint8 E4M3 codes (dtype FP8).  ``rows``: query rows to evaluate (all
+    when None).  Returns (o [B,len(rows),H,d_v], lse [B,H,len(rows)]) float64.
+    """
+    lib = _load()
+    want = np.uint16 if dtype == BF16 else np.uint8
+    q = np.ascontiguousarray(q, dtype=want)
+    k = np.ascontiguousarray(k, dtype=want)
+    v = np.ascontiguousarray(v, dtype=want)
+    B, S, H, dqk = q.shape
+    dv = v.shape[3]
+    assert k.shape == (B, S, H, dqk) and v.shape[:3] == (B, S, H)
+    rows = np.arange(S, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    o = np.empty((B, rows.size, H, dv), np.float64)
+    lse = np.empty((B, H, rows.size), np.float64)
+    rc = lib.oracle_attn(_ptr(q), _ptr(k), _ptr(v), dtype, q_descale, k_descale, v_descale,
+                         B, S, H, dqk, dv, float(tau), int(bool(causal)), _ptr(rows), rows.size,
+                         _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_attn rejected its arguments")
+    return o, lse
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
