@@ -1,0 +1,180 @@
+"""Benchmark: causal prefill attention forward TFLOP/s on one MI355X.
+
+One step = one attn_fwd call over the whole workload (every query block of
+every head), inputs resident in HBM.  Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload C4] [--gpus 1]
+                  [--cpu-seconds 12] [--no-cpu]
+
+Workloads (seeded synthetic inputs, recipes in causal_prefill_attention_attn_amd/synth.py):
+  C4  (default) FP8 e4m3, B1 H32 S32768 d128, LLM-like activations
+  C4g FP8 e4m3, B1 H32 S32768 d128, N(0,1)
+  C5  FP8 e4m3 MLA, B1 H16 S32768 d_qk192 d_v128, N(0,1)
+  C3  FP8 e4m3, B1 H32 S16384 d128, N(0,1)
+  C2  BF16, B1 H32 S4096 d128, N(0,1)
+  C2x BF16, B1 H32 S32768 d128, N(0,1)
+FLOPs per step: B*H*S^2*(d_qk+d_v) (both products over the causal half).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C4")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def device_inputs(w, torch, pkg, synth):
+    """Seeded inputs on the device: bf16, or e4m3 codes quantized by the library."""
+    qf, kf, vf = synth.generate(w)
+    dev = torch.device("cuda:0")
+    if w.dtype == synth.BF16:
+        t = [torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (qf, kf, vf)]
+        return t, [1.0, 1.0, 1.0], (qf, kf, vf)
+    t, ds = [], []
+    for x in (qf, kf, vf):
+        codes, d = pkg.quantize_fp8(torch.from_numpy(x).to(dev))
+        t.append(codes)
+        ds.append(d)
+    torch.cuda.synchronize()
+    return t, ds, (qf, kf, vf)
+
+
+def cpu_baseline(w, host, seconds, synth):
+    """Time the fp64 oracle on a bounded sample of the same workload: a growing
+    set of query rows of head 0, until about `seconds` of CPU work."""
+    import oracle
+    oracle.build()
+    qf, kf, vf = host
+    h = 0
+    if w.dtype == synth.BF16:
+        enc = [synth.to_bf16_bits(np.ascontiguousarray(x[:, :, h:h + 1])) for x in (qf, kf, vf)]
+        ds = [1.0, 1.0, 1.0]
+    else:
+        ds = [oracle.descale_amax(x) for x in (qf, kf, vf)]
+        enc = [oracle.quantize_e4m3(np.ascontiguousarray(x[:, :, h:h + 1]), d)
+               for x, d in zip((qf, kf, vf), ds)]
+    rng = np.random.default_rng(4242)
+    n, spent, flops, nrows = 8, 0.0, 0.0, 0
+    while spent < seconds and nrows < w.S:
+        rows = np.sort(rng.choice(w.S, size=min(n, w.S), replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention(enc[0], enc[1], enc[2], w.dtype, w.softmax_scale, True, rows=rows,
+                         q_descale=ds[0], k_descale=ds[1], v_descale=ds[2])
+        spent += time.perf_counter() - t0
+        flops += float(np.sum(rows + 1)) * (w.d_qk + w.d_v) * 2.0 * w.B
+        nrows += rows.size
+        n *= 2
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d uniformly drawn query rows of head 0 (batch %d) of %s, causal, "
+                      "fp64 oracle, %.1f s" % (nrows, w.B, w.name, spent)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the kernel runs on one device and "
+              "multi-GPU runs are not part of this library; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import causal_prefill_attention_attn_amd as pkg
+    from causal_prefill_attention_attn_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dtname = "bf16" if w.dtype == synth.BF16 else "fp8"
+    log("bench: workload %s (%s)" % (w.name, w.description))
+    t, ds, host = device_inputs(w, torch, pkg, synth)
+    dev = t[0].device
+    o = torch.empty((w.B, w.S, w.H, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        pkg.flash_attn_func(t[0], t[1], t[2], softmax_scale=w.softmax_scale, causal=True,
+                            q_descale=ds[0], k_descale=ds[1], v_descale=ds[2], out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_step = wall * 1e3 / args.steps
+    flops = w.causal_flops
+    value = flops / (ms_step * 1e-3) / 1e12
+    avg_kern = float(np.mean(kern_ms))
+    achieved = flops / (avg_kern * 1e-3) / 1e12
+    log("bench: %d steps, wall %.3f ms/step, kernel mean %.3f ms (median %.3f, min %.3f)"
+        % (args.steps, ms_step, avg_kern, float(np.median(kern_ms)), float(np.min(kern_ms))))
+
+    esz = 2 if w.dtype == synth.BF16 else 1
+    rows = w.B * w.S * w.H
+    compulsory = rows * (2 * w.d_qk + w.d_v) * esz + rows * w.d_v * 2 + w.B * w.H * w.S * 4
+    out = {
+        "metric": "causal prefill attention TFLOP/s (FP8 & BF16) and % of MFMA peak at 32K",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtname,
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "B": w.B, "H": w.H,
+                   "S": w.S, "d_qk": w.d_qk, "d_v": w.d_v, "causal": True,
+                   "softmax_scale": w.softmax_scale, "flops_per_step": flops,
+                   "frac_of_peak": round(value / PEAK_TFLOPS[dtname], 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_TFLOPS[dtname], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS[dtname], 4), "traffic": None,
+                     "kernel": "attn_fwd_%s_kernel<%d>" % (dtname, w.d_qk),
+                     "kernel_ms_mean": round(avg_kern, 4),
+                     "compulsory_bytes": compulsory},
+    }
+    if not args.no_cpu:
+        log("bench: timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+"""MI355X (gfx950) causal prefill attention forward: Python binding.
+
+This module only marshals arguments to the C ABI declared in
+``include/attn.h`` (``libcpattn.so``, built in-tree by ``_build.py``).  Every
+step of the computation runs in the library's HIP kernels; PyTorch supplies
+device memory and the current stream.  There is no fallback: if the library
+is missing or was built without a usable GPU, calls raise.
+
+The operation is causal forward (prefill) attention in FP8 e4m3 and BF16 at
+head dimension 128 and in the MLA 192/128 shape behind a flash_attn_func
+style call, as the ZYFA pages describe it ("TL;DR" on the acheiumaia.com.br
+page; "Ce que couvrent les noyaux" on the ai-daily-news.org page).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "ATTN_DTYPE_BF16", "ATTN_DTYPE_FP8", "AttnError", "lib_path", "load_library",
+    "attn_fwd", "attn_amax_f32", "attn_quantize_e4m3", "attn_status_string", "attn_version",
+    "flash_attn_func", "quantize_fp8",
+]
+
+ATTN_DTYPE_BF16 = 0
+ATTN_DTYPE_FP8 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libcpattn.so")
+_lib = None
+
+
+class AttnError(ValueError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: status %d (%s)" % (where, status, attn_status_string(status)))
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libcpattn.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise OSError("libcpattn.so is not built; run __graft_entry__.build() or "
+                      "python -m causal_prefill_attention_attn_amd._build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.attn_version.restype = i32
+    lib.attn_version.argtypes = []
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32,
+                             f32, f32, f32, vp]
+    lib.attn_amax_f32.restype = i32
+    lib.attn_amax_f32.argtypes = [vp, i64, vp, vp]
+    lib.attn_quantize_e4m3.restype = i32
+    lib.attn_quantize_e4m3.argtypes = [vp, i64, f32, vp, vp]
+    _lib = lib
+    return lib
+
+
+def attn_version() -> int:
+    return int(load_library().attn_version())
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+# ----------------------------------------------------------- raw C-ABI calls
+def attn_fwd(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale, causal, dtype,
+             q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None) -> int:
+    """Direct call of the C function on integer addresses; returns the status."""
+    return int(load_library().attn_fwd(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale,
+                                       causal, dtype, q_descale, k_descale, v_descale, stream))
+
+
+def attn_amax_f32(x, n, amax_out, stream=None) -> int:
+    return int(load_library().attn_amax_f32(x, n, amax_out, stream))
+
+
+def attn_quantize_e4m3(x, n, descale, out, stream=None) -> int:
+    return int(load_library().attn_quantize_e4m3(x, n, descale, out, stream))
+
+
+# ------------------------------------------------------------ torch helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise AttnError(status, where)
+
+
+def _element_dtype(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return ATTN_DTYPE_FP8
+    raise TypeError("q, k, v must be bfloat16, float8_e4m3fn or uint8 (e4m3 codes), got %s"
+                    % t.dtype)
+
+
+def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_descale=1.0,
+                    v_descale=1.0, out=None, lse=None, return_lse=True):
+    """Forward attention on [B, S, H, D] tensors.
+
+    q, k: [B, S, H, d_qk]; v: [B, S, H, d_v]; all bfloat16, or all FP8 e4m3
+    (``torch.float8_e4m3fn`` or uint8 codes) with per-tensor descales.
+    Returns ``(o, lse)``: o bfloat16 [B, S, H, d_v], lse float32 [B, H, S]
+    (natural log); lse is None when ``return_lse`` is False.
+    """
+    torch = _torch()
+    dt = _element_dtype(q)
+    if _element_dtype(k) != dt or _element_dtype(v) != dt:
+        raise TypeError("q, k and v must share one element type")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous 4-D [B, S, H, D] CUDA tensor" % name)
+    B, S, H, d_qk = q.shape
+    d_v = v.shape[3]
+    if tuple(k.shape) != (B, S, H, d_qk) or tuple(v.shape[:3]) != (B, S, H):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                             tuple(v.shape)))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_qk)
+    if out is None:
+        out = torch.empty((B, S, H, d_v), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                  lse.data_ptr() if lse is not None else None, B, S, H, d_qk, d_v,
+                  float(softmax_scale), int(bool(causal)), dt, float(q_descale),
+                  float(k_descale), float(v_descale), _stream_handle(q.device))
+    _check(st, "attn_fwd")
+    return out, lse
+
+
+def quantize_fp8(x):
+    """Per-tensor E4M3FN quantization on the GPU: returns (codes uint8, descale)
+    with descale = amax / 448 computed in fp32 (1.0 for an all-zero tensor)."""
+    torch = _torch()
+    import numpy as np
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    n = x.numel()
+    amax = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _check(attn_amax_f32(x.data_ptr(), n, amax.data_ptr(), _stream_handle(x.device)),
+           "attn_amax_f32")
+    a = np.float32(amax.item())
+    descale = float(a / np.float32(448.0)) if a > 0 else 1.0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(attn_quantize_e4m3(x.data_ptr(), n, descale, codes.data_ptr(),
+                              _stream_handle(x.device)), "attn_quantize_e4m3")
+    return codes, descale

@@ -1,0 +1,104 @@
+// C-ABI front end: argument validation (host only, before any HIP call),
+// instance selection and launch.  The declarations and their contract are in
+// include/attn.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "attn_kernels.h"
+
+namespace {
+
+bool finite_positive(float x) { return isfinite(x) && x > 0.0f; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// half-open byte ranges [p, p + n) overlap
+bool overlap(const void* p, int64_t np, const void* q, int64_t nq) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + (uintptr_t)nq && b < a + (uintptr_t)np;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return 100; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, S and H must be >= 1 and the problem must fit 32-bit grid indexing";
+    case ATTN_ERR_DTYPE: return "dtype must be ATTN_DTYPE_BF16 (0) or ATTN_DTYPE_FP8 (1)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported (d_qk, d_v) (want (128,128) or (192,128)) or causal not 0/1";
+    case ATTN_ERR_SCALE: return "softmax_scale and the FP8 descales must be finite and > 0";
+    case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case ATTN_ERR_ALIAS: return "o or lse overlaps an input or the other output";
+    case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+             int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale, int causal, int dtype,
+             float q_descale, float k_descale, float v_descale, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (B < 1 || S < 1 || H < 1) return ATTN_ERR_SHAPE;
+  // 32-bit indices inside the kernels: rows, heads, batch*head and the grid
+  if (S > INT32_MAX || H > INT32_MAX || B > INT32_MAX || B * H > INT32_MAX) return ATTN_ERR_SHAPE;
+  const int64_t nqb = (S + 127) / 128;
+  if (nqb * B * H > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8) return ATTN_ERR_DTYPE;
+  if (!((d_qk == 128 || d_qk == 192) && d_v == 128) || (causal != 0 && causal != 1))
+    return ATTN_ERR_UNSUPPORTED;
+  if (!finite_positive(softmax_scale)) return ATTN_ERR_SCALE;
+  if (dtype == ATTN_DTYPE_FP8 &&
+      !(finite_positive(q_descale) && finite_positive(k_descale) && finite_positive(v_descale)))
+    return ATTN_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return ATTN_ERR_ALIGN;
+  const int64_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 1;
+  const int64_t rows = B * S * H;
+  const int64_t nq = rows * d_qk * esz, nv = rows * d_v * esz, no = rows * d_v * 2;
+  const int64_t nl = B * H * S * 4;
+  if (overlap(o, no, q, nq) || overlap(o, no, k, nq) || overlap(o, no, v, nv)) return ATTN_ERR_ALIAS;
+  if (lse && (overlap(lse, nl, q, nq) || overlap(lse, nl, k, nq) || overlap(lse, nl, v, nv) ||
+              overlap(lse, nl, o, no)))
+    return ATTN_ERR_ALIAS;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int rc;
+  if (dtype == ATTN_DTYPE_BF16)
+    rc = cpattn::launch_attn_bf16(q, k, v, o, lse, (int)B, (int)S, (int)H, d_qk, softmax_scale,
+                                  causal, st);
+  else
+    rc = cpattn::launch_attn_fp8(q, k, v, o, lse, (int)B, (int)S, (int)H, d_qk, softmax_scale,
+                                 causal, q_descale, k_descale, v_descale, st);
+  return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_amax_f32(const float* x, int64_t n, float* amax_out, void* stream) {
+  if (!x || !amax_out) return ATTN_ERR_NULL;
+  if (n < 1) return ATTN_ERR_SHAPE;
+  if (!aligned(x, 4) || !aligned(amax_out, 4)) return ATTN_ERR_ALIGN;
+  if (overlap(amax_out, 4, x, n * 4)) return ATTN_ERR_ALIAS;
+  return cpattn::launch_amax_f32(x, n, amax_out, reinterpret_cast<hipStream_t>(stream)) == 0
+             ? ATTN_OK
+             : ATTN_ERR_LAUNCH;
+}
+
+int attn_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out, void* stream) {
+  if (!x || !out) return ATTN_ERR_NULL;
+  if (n < 1) return ATTN_ERR_SHAPE;
+  if (!finite_positive(descale)) return ATTN_ERR_SCALE;
+  if (!aligned(x, 4)) return ATTN_ERR_ALIGN;
+  if (overlap(out, n, x, n * 4)) return ATTN_ERR_ALIAS;
+  return cpattn::launch_quantize_e4m3(x, n, descale, out, reinterpret_cast<hipStream_t>(stream)) == 0
+             ? ATTN_OK
+             : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

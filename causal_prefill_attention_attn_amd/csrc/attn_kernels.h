@@ -1,0 +1,23 @@
+// Internal launchers shared by the C-ABI front end (attn_api.hip) and the
+// kernel translation units.  Arguments are already validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+// BF16 q/k/v, d_qk in {128, 192}, d_v = 128.  Returns 0 or -1 (launch error).
+int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int S, int H, int d_qk, float softmax_scale, int causal,
+                     hipStream_t stream);
+
+// FP8 E4M3FN q/k/v with per-tensor descales, d_qk in {128, 192}, d_v = 128.
+int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int S, int H, int d_qk, float softmax_scale, int causal, float q_descale,
+                    float k_descale, float v_descale, hipStream_t stream);
+
+int launch_amax_f32(const float* x, int64_t n, float* amax_out, hipStream_t stream);
+int launch_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out,
+                         hipStream_t stream);
+
+}  // namespace cpattn

@@ -1,0 +1,80 @@
+// Per-tensor FP8 quantization helpers: amax and fp32 -> E4M3FN.
+//
+// Most of the FP8 error of the attention comes from rounding Q, K and V to
+// FP8 ("Precisao, estabilidade e efeito na pratica" on the
+// miraibroadcast.com page); these kernels produce the e4m3 codes and the
+// per-tensor scale that attn_fwd consumes.  The encoder works on the fp32
+// bit pattern: exponent re-bias plus round-to-nearest-even on the dropped
+// mantissa bits for normal results, an exact multiply by 2^9 and rint for
+// the subnormal range, and saturation to the largest finite code (448).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_kernels.h"
+
+namespace cpattn {
+namespace {
+
+__global__ void zero_u32(uint32_t* p) { *p = 0u; }
+
+__global__ void __launch_bounds__(256) amax_kernel(const float* __restrict__ x, int64_t n,
+                                                   uint32_t* __restrict__ out) {
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    m = fmaxf(m, fabsf(x[i]));  // fmaxf drops NaN operands
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    // non-negative floats order like their bit patterns: max is exact and order-free
+    atomicMax(out, __float_as_uint(m));
+  }
+}
+
+__device__ __forceinline__ uint8_t e4m3_from_f32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7f;                 // NaN
+  if (a >= 0x43e00000u) return (uint8_t)(sign | 0x7e);  // |x| >= 448 (incl. inf): saturate
+  if (a < 0x3c800000u) {                            // |x| < 2^-6: multiples of 2^-9
+    const float m = rintf(__uint_as_float(a) * 512.0f);  // exact scaling, RNE
+    return (uint8_t)(sign | (uint32_t)m);           // m == 8 is the code of 2^-6
+  }
+  // normal: keep 3 of 23 mantissa bits, round half to even, re-bias 127 -> 7
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+  const uint32_t code = (r >> 20) - ((127u - 7u) << 3);
+  return (uint8_t)(sign | (code > 0x7eu ? 0x7eu : code));
+}
+
+__global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ x, int64_t n,
+                                                       float descale, uint8_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = e4m3_from_f32(x[i] / descale);
+}
+
+}  // namespace
+
+int launch_amax_f32(const float* x, int64_t n, float* amax_out, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_u32, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(amax_out));
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n,
+                     reinterpret_cast<uint32_t*>(amax_out));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out,
+                         hipStream_t stream) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, descale,
+                     out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace cpattn

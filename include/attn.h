@@ -1,0 +1,128 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) causal prefill attention library.
+ *
+ * One forward operation:
+ *
+ *   O = softmax(tau * Q K^T + causal mask) V,     lse_i = log sum_j exp(s_ij)
+ *
+ * in BF16 or FP8 (OCP E4M3FN) inputs, for head dimension 128 and for the
+ * DeepSeek-V2 latent-attention shape (QK dimension 192, V dimension 128).
+ *
+ * Source of the operation: the ZYFA announcement pages describe causal
+ * forward (prefill) attention kernels in FP8 e4m3 and BF16 at head dimension
+ * 128 and in the MLA 192/128 shape, exposed through a flash_attn_func style
+ * call ("TL;DR" and "O que e o ZYFA?" on the acheiumaia.com.br page; "Ce que
+ * couvrent les noyaux" on the ai-daily-news.org page), whose core is the two
+ * matrix products Q.K^T and P.V with a softmax between them ("Por que a
+ * atencao FP8 tem desempenho inferior no MI355X?" on the acheiumaia.com.br
+ * page).  The pages print no formula; the one above is the textbook
+ * definition of softmax attention with a causal mask.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked "device" must be device memory (hipMalloc or a torch
+ *     CUDA tensor); the caller owns every buffer.  The library allocates no
+ *     device memory and keeps no mutable global state; calls are re-entrant.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued on it and the call returns without synchronizing; a return of
+ *     ATTN_OK means "validated and enqueued".
+ *   - Every argument check happens on the host before any HIP call.  A
+ *     negative return means nothing was enqueued and no memory was touched.
+ */
+#ifndef CPATTN_ATTN_H
+#define CPATTN_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define ATTN_OK 0
+#define ATTN_ERR_NULL (-1)        /* a required pointer is NULL */
+#define ATTN_ERR_SHAPE (-2)       /* B, S or H < 1, or a size overflows */
+#define ATTN_ERR_DTYPE (-3)       /* dtype is not ATTN_DTYPE_BF16 / ATTN_DTYPE_FP8 */
+#define ATTN_ERR_UNSUPPORTED (-4) /* (d_qk, d_v) not in {(128,128), (192,128)}, or causal not 0/1 */
+#define ATTN_ERR_SCALE (-5)       /* softmax_scale or a descale not finite and > 0 */
+#define ATTN_ERR_ALIGN (-6)       /* a pointer is not 16-byte aligned */
+#define ATTN_ERR_ALIAS (-7)       /* an output buffer overlaps an input or the other output */
+#define ATTN_ERR_LAUNCH (-8)      /* the HIP runtime rejected the kernel launch */
+
+/* element types of q, k, v */
+#define ATTN_DTYPE_BF16 0 /* bfloat16 */
+#define ATTN_DTYPE_FP8 1  /* OCP FP8 E4M3FN (bias 7, max 448, no inf) */
+
+/* Library version, major*10000 + minor*100 + patch. */
+int attn_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/*
+ * attn_fwd -- causal (or full) softmax attention, forward only.
+ *
+ * Operation (one independent problem per batch b and head h):
+ *   qhat = q            (BF16)     or  decode_e4m3(q) * q_descale   (FP8)
+ *   khat, vhat likewise with k_descale, v_descale
+ *   s_ij  = softmax_scale * <qhat[b,i,h,:], khat[b,j,h,:]>
+ *   key j is visible from query i iff (causal ? j <= i : 1)
+ *   o[b,i,h,:]  = sum_visible softmax_j(s_ij) * vhat[b,j,h,:]   (rounded to bf16)
+ *   lse[b,h,i]  = ln sum_visible exp(s_ij)                      (fp32)
+ * The FP8 path rounds the probabilities to E4M3 before the P.V product,
+ * after scaling each 64-key block of a row by a power of two, and removes
+ * the factor inside the scaled matrix instruction (the block-scaling
+ * technique in "Como o motor de atencao FP8 da Zyphra funciona" on the
+ * miraibroadcast.com page); the row sum uses the rounded probabilities.
+ *
+ * Arguments:
+ *   q    device, [B, S, H, d_qk] contiguous, bf16 or e4m3 codes
+ *   k    device, [B, S, H, d_qk] contiguous, same type as q
+ *   v    device, [B, S, H, d_v]  contiguous, same type as q
+ *   o    device, [B, S, H, d_v]  contiguous, bf16 (written)
+ *   lse  device, [B, H, S] contiguous, fp32 natural-log LSE (written);
+ *        may be NULL to skip it
+ *   B, S, H        >= 1 (S need not be a multiple of any tile size)
+ *   d_qk, d_v      (128, 128) or (192, 128)
+ *   softmax_scale  tau, finite and > 0 (callers usually pass 1/sqrt(d_qk))
+ *   causal         1 = causal mask (j <= i), 0 = no mask
+ *   dtype          ATTN_DTYPE_BF16 or ATTN_DTYPE_FP8
+ *   q/k/v_descale  FP8 only: per-tensor dequantization factors, finite and
+ *                  > 0 (ignored for BF16)
+ *   stream         hipStream_t or NULL
+ * Pointers must be 16-byte aligned; o and lse must not overlap q, k, v or
+ * each other.  Repeated calls on the same inputs give bitwise identical o
+ * and lse (no atomics, fixed reduction order).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+             int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale, int causal, int dtype,
+             float q_descale, float k_descale, float v_descale, void* stream);
+
+/*
+ * attn_amax_f32 -- largest magnitude of a float32 tensor, for choosing the
+ * per-tensor FP8 descale (amax / 448).  The pages attribute most of the FP8
+ * error to this quantization of Q, K and V ("Precisao, estabilidade e
+ * efeito na pratica" on the miraibroadcast.com page).
+ *   x         device, n float32 values (NaN entries are ignored)
+ *   n         >= 1
+ *   amax_out  device, one float32 (written; overwritten, not accumulated)
+ * The result is exact and independent of the launch (max is order-free).
+ */
+int attn_amax_f32(const float* x, int64_t n, float* amax_out, void* stream);
+
+/*
+ * attn_quantize_e4m3 -- out[i] = E4M3FN(fp32(x[i] / descale)): one IEEE
+ * fp32 division, then round-to-nearest-even into E4M3FN, saturating
+ * magnitudes above 448 to +-448 (never NaN from finite input; NaN maps to
+ * 0x7F).
+ *   x        device, n float32 values
+ *   n        >= 1
+ *   descale  finite and > 0
+ *   out      device, n bytes (written); must not overlap x
+ */
+int attn_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_ATTN_H */

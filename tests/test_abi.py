@@ -1,0 +1,95 @@
+"""The C-ABI library builds, loads and exports what include/attn.h declares,
+and rejects bad arguments on the host before any HIP call.
+
+Every call here fails validation, so no kernel is launched and no GPU is
+needed; the pointers are made-up aligned addresses that are never touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_prefill_attention_attn_amd as pkg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkg.lib_path()):
+        from causal_prefill_attention_attn_amd import _build
+        _build.build()
+    return pkg.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted(["attn_version", "attn_status_string", "attn_fwd", "attn_amax_f32",
+                            "attn_quantize_e4m3"]), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert pkg.attn_version() >= 100
+    for code in range(0, -9, -1):
+        s = pkg.attn_status_string(code)
+        assert s and s != "unknown status"
+    assert pkg.attn_status_string(-100) == "unknown status"
+
+
+# made-up, 256-byte aligned, far apart addresses (never dereferenced)
+Q, K, V, O, L = (0x10000000 * (i + 1) for i in range(5))
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, S=256, H=2, d_qk=128, d_v=128, softmax_scale=0.088,
+            causal=1, dtype=0, q_descale=1.0, k_descale=1.0, v_descale=1.0, stream=None)
+
+
+def _call(**over):
+    a = dict(GOOD)
+    a.update(over)
+    return pkg.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["S"], a["H"],
+                        a["d_qk"], a["d_v"], a["softmax_scale"], a["causal"], a["dtype"],
+                        a["q_descale"], a["k_descale"], a["v_descale"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(B=0), -2), (dict(S=0), -2), (dict(H=-1), -2), (dict(S=2 ** 31), -2),
+    (dict(B=2 ** 20, H=2 ** 12), -2),
+    (dict(dtype=2), -3), (dict(dtype=-1), -3),
+    (dict(d_qk=64), -4), (dict(d_v=192), -4), (dict(d_qk=192, d_v=192), -4), (dict(causal=2), -4),
+    (dict(softmax_scale=0.0), -5), (dict(softmax_scale=float("inf")), -5),
+    (dict(softmax_scale=float("nan")), -5), (dict(softmax_scale=-1.0), -5),
+    (dict(dtype=1, q_descale=0.0), -5), (dict(dtype=1, v_descale=float("nan")), -5),
+    (dict(q=Q + 8), -6), (dict(o=O + 2), -6), (dict(lse=L + 2), -6),
+    (dict(o=Q), -7), (dict(o=K + 256), -7), (dict(lse=V + 64), -7), (dict(lse=O + 1024), -7),
+])
+def test_attn_fwd_rejects(lib, over, code):
+    assert _call(**over) == code
+
+
+def test_bf16_ignores_descales_fp8_checks_them(lib):
+    # a BF16 call with invalid descales is still rejected only for its real fault
+    assert _call(q_descale=float("nan"), d_qk=64) == -4
+
+
+def test_quant_entry_points_reject(lib):
+    assert pkg.attn_amax_f32(None, 10, O) == -1
+    assert pkg.attn_amax_f32(Q, 0, O) == -2
+    assert pkg.attn_amax_f32(Q, 10, Q + 4) == -7
+    assert pkg.attn_quantize_e4m3(Q, 10, 0.0, O) == -5
+    assert pkg.attn_quantize_e4m3(Q, 10, 1.0, None) == -1
+    assert pkg.attn_quantize_e4m3(Q, 0, 1.0, O) == -2
+    assert pkg.attn_quantize_e4m3(Q, 16, 1.0, Q + 8) == -7
