@@ -1,8 +1,359 @@
+// FP8 (OCP E4M3FN) causal prefill attention forward for gfx950 (CDNA4).
+//
+// Both products run on v_mfma_scale_f32_32x32x64_f8f6f4, the FP8 matrix
+// path that runs at twice the BF16 rate; the softmax between them runs on
+// the vector unit at the same speed in either precision ("Por que a atencao
+// FP8 tem desempenho inferior no MI355X?" on the acheiumaia.com.br page).
+// Work is organised per wave as 32 queries against the keys of a tile, the
+// unit the pages cost (same section).
+//
+// Per wave (32 query rows), per 128-key tile:
+//   S^T = K . Q^T   A = K rows (one key per lane column), B = Q^T (one query
+//                   per lane column), 32 bytes of the head dimension per
+//                   lane per step.  Lane l of the result holds query l%32 and
+//                   16 keys of each 32-key block, so row maxima are in-lane
+//                   plus one exchange between lane halves.
+//   P               each 64-key block of a row is scaled by a power of two
+//                   2^k before rounding to e4m3, with k chosen from the
+//                   block's largest score so the block maximum lands in
+//                   (128, 256]; the scale is removed inside the scaled
+//                   matrix instruction through its E8M0 operand (the block
+//                   scaling of "Como o motor de atencao FP8 da Zyphra
+//                   funciona" on the miraibroadcast.com page).  In the
+//                   32x32x64 instruction a lane's scale covers the 32-key
+//                   block held by bytes 0-15 (or 16-31) of both lane halves,
+//                   so both halves carry the same 64-key exponent.
+//   l               the row sum is taken from the rounded, de-scaled P that
+//                   enters P.V, with one extra matrix instruction per 64-key
+//                   block that multiplies P^T by a block of ones (same
+//                   section of that page).
+//   O^T += V^T.P^T  A = V^T read from a row-major V tile in LDS with
+//                   ds_read_b64_tr_b8 (16 lanes cooperatively read 8 rows of
+//                   16 bytes and each receives one column), B = P^T straight
+//                   from registers.
+// The running max m is refreshed when some row of the wave sees a larger
+// tile maximum (rescale skipped otherwise).  With m equal to the row max,
+// the row's largest probability becomes exactly 2^8 before rounding, so the
+// dominant weight of peaked rows is exact in e4m3.  A refresh threshold
+// (lazy_log2 > 0) skips rescales while the new maximum stays within
+// 2^lazy_log2 of m; the per-block exponent absorbs the excess, so results
+// stay correct but the top weight is no longer exact (larger error on
+// peaked rows).
 #include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
 #include "attn_kernels.h"
+
 namespace cpattn {
-int launch_attn_fp8(const void*, const void*, const void*, void*, float*, int, int, int, int, float,
-                    int, float, float, float, hipStream_t) {
-  return -1;
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;   // query rows per workgroup
+constexpr int kBN = 128;           // keys per tile (two 64-key scale blocks)
+constexpr int kDV = 128;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kE8M0One = 127;      // E8M0 encoding of 2^0
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int scale_a, int scale_b) {
+  // operand formats 0/0 = E4M3 x E4M3; op_sel 0 = byte 0 of each scale VGPR
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+// 16-byte chunk swizzle of a V row (128 bytes = 8 chunks) so that the eight
+// key rows one ds_read_b64_tr_b8 touches fall in distinct LDS banks
+__device__ __forceinline__ int v_swz(int key) { return ((key >> 1) & 1) * 2 + ((key >> 3) & 1) * 4; }
+
+// key (offset inside a 64-key block) whose probability sits in byte e of the
+// P^T operand of lane half h: byte e < 16 comes from S block 0 register e,
+// e >= 16 from S block 1 register e-16
+__device__ __forceinline__ int p_key(int h, int e) {
+  return (e >> 4) * 32 + ((e & 15) >> 2) * 8 + h * 4 + (e & 3);
+}
+
+template <int DQK>
+struct Smem {
+  static constexpr int kPitch = DQK + 16;  // bytes per K row (+16 B breaks bank aliasing)
+  uint8_t k[kBN * kPitch];
+  uint8_t v[kBN * kDV];                    // row-major, chunk-swizzled
+};
+
+template <int DQK>
+__global__ void __launch_bounds__(kThreads, 2)
+attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+                    const uint8_t* __restrict__ v, __bf16* __restrict__ o,
+                    float* __restrict__ lse, int S, int H, int BH, int nqb, float c_log2,
+                    float v_descale, int causal, float lazy_log2) {
+  constexpr int kSteps = DQK / 64;                 // 32x32x64 steps of Q.K^T
+  constexpr int kKRowChunks = DQK / 16;            // 16-byte chunks per K row
+  constexpr int kKChunks = kBN * kKRowChunks / kThreads;
+  constexpr int kVChunks = kBN * (kDV / 16) / kThreads;
+  static_assert(kBN * kKRowChunks % kThreads == 0 && kBN * (kDV / 16) % kThreads == 0, "split");
+  using SM = Smem<DQK>;
+  __shared__ __attribute__((aligned(16))) SM sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  const int id = blockIdx.x;
+  const int qb = nqb - 1 - id / BH;  // longest rows first
+  const int bh = id % BH;
+  const int b = bh / H;
+  const int h = bh % H;
+  const int q0 = qb * kBM;
+  const int q0w = q0 + wave * 32;
+  const int64_t rsQK = (int64_t)H * DQK;
+  const int64_t rsV = (int64_t)H * kDV;
+  const uint8_t* qbh = q + ((int64_t)b * S * H + h) * DQK;
+  const uint8_t* kbh = k + ((int64_t)b * S * H + h) * DQK;
+  const uint8_t* vbh = v + ((int64_t)b * S * H + h) * kDV;
+
+  // ---- Q^T operand: lane (query col, half) holds d = s*64 + half*32 .. +31
+  i32x8 qreg[kSteps];
+  {
+    const int qi = q0w + col;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      if (qi < S) {
+        const uint4* p = reinterpret_cast<const uint4*>(qbh + qi * rsQK + s * 64 + half * 32);
+        const uint4 x0 = p[0], x1 = p[1];
+        qreg[s] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                        (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      } else {
+        qreg[s] = i32x8{};
+      }
+    }
+  }
+
+  const int nkt_all = (S + kBN - 1) / kBN;
+  const int nkt = causal ? min(nkt_all, (q0 + kBM - 1) / kBN + 1) : nkt_all;
+
+  uint4 kst[kKChunks];
+  uint4 vst[kVChunks];
+  auto load_tile = [&](int t) {
+    const int key0 = t * kBN;
+#pragma unroll
+    for (int j = 0; j < kKChunks; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c / kKRowChunks, cc = c % kKRowChunks;
+      const int key = key0 + r;
+      kst[j] = key < S ? *reinterpret_cast<const uint4*>(kbh + key * rsQK + cc * 16)
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kVChunks; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c >> 3, cc = c & 7;
+      const int key = key0 + r;
+      vst[j] = key < S ? *reinterpret_cast<const uint4*>(vbh + key * rsV + cc * 16)
+                       : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int j = 0; j < kKChunks; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c / kKRowChunks, cc = c % kKRowChunks;
+      *reinterpret_cast<uint4*>(&sm.k[r * SM::kPitch + cc * 16]) = kst[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kVChunks; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c >> 3, cc = c & 7;
+      *reinterpret_cast<uint4*>(&sm.v[r * kDV + ((cc ^ v_swz(r)) << 4)]) = vst[j];
+    }
+  };
+
+  // per-lane LDS byte offsets of the V^T operand reads (independent of the tile):
+  // lane i of a 16-lane group supplies row i/2 (a key) and byte half i%2 of a
+  // 16-byte dv chunk; the group's dv chunk is (db*2 + (lane/16)%2)
+  const int gi = lane & 15;
+  const int dvhalf = (lane >> 4) & 1;
+  // voff: row base + byte half; vswz: the row's chunk swizzle (the chunk
+  // index d*2 + dvhalf is applied per value block in the loop)
+  int voff[2][4];  // [64-key block][8-byte group of the operand]
+  int vswz[2][4];
+#pragma unroll
+  for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int key = ch * 64 + p_key(half, t4 * 8 + (gi >> 1));
+      voff[ch][t4] = key * kDV + (gi & 1) * 8;
+      vswz[ch][t4] = v_swz(key);
+    }
+
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+
+  f32x16 oacc[kDV / 32];
+#pragma unroll
+  for (int i = 0; i < kDV / 32; ++i) oacc[i] = f32x16{};
+  f32x16 lacc = f32x16{};   // every entry of a column holds the same row sum
+  float m_run = -INFINITY;  // max of c*s in use (log2 domain)
+
+  if (nkt > 0) load_tile(0);
+  for (int t = 0; t < nkt; ++t) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (t + 1 < nkt) load_tile(t + 1);
+
+    const int key0 = t * kBN;
+    if (causal && key0 > q0w + 31) continue;
+
+    // ---- S^T = K . Q^T, four 32-key blocks
+    f32x16 sacc[kBN / 32];
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb) {
+      sacc[kb] = f32x16{};
+      const uint8_t* krow = &sm.k[(kb * 32 + col) * SM::kPitch + half * 32];
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(krow + s * 64);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(krow + s * 64 + 16);
+        const i32x8 a = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                         (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        sacc[kb] = mfma_f8(a, qreg[s], sacc[kb], kE8M0One, kE8M0One);
+      }
+    }
+
+    // ---- mask on diagonal / ragged tiles
+    const int qi = q0w + col;
+    if ((causal && key0 + kBN - 1 > q0w) || key0 + kBN > S) {
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          if (key >= S || (causal && key > qi)) sacc[kb][i] = -INFINITY;
+        }
+    }
+
+    // ---- block maxima (64 keys = two S blocks, both lane halves)
+    float bmax[2];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[2 * ch][i], sacc[2 * ch + 1][i]));
+      bmax[ch] = pair_max(mx) * c_log2;
+    }
+    const float tmax = fmaxf(bmax[0], bmax[1]);
+    if (__any(tmax > m_run + lazy_log2)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < kDV / 32; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      lacc[0] *= alpha;
+    }
+
+    // ---- P = e4m3(2^(c*s - m + k_blk)), scale 2^-k_blk in E8M0
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      // k = 8 - ceil(block max - m) puts the block maximum in (2^7, 2^8]
+      // (k >= 0 since block max - m <= lazy_log2 <= 8)
+      float kf = 8.0f - __builtin_ceilf(bmax[ch] - m_run);
+      kf = fminf(kf, 126.0f);
+      const float ofs = kf - m_run;
+      const int pscale = kE8M0One - (int)kf;
+      i32x8 pw;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = 2 * ch + (w >> 2);
+        const int i0 = (w & 3) * 4;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 0], c_log2, ofs));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 1], c_log2, ofs));
+        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 2], c_log2, ofs));
+        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 3], c_log2, ofs));
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+        pw[w] = word;
+      }
+      // ---- O^T += V^T . P^T over this 64-key block, and l += ones . P^T
+#pragma unroll
+      for (int d = 0; d < kDV / 32; ++d) {
+        const int cidx = d * 2 + dvhalf;
+        i32x8 a;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const uint8_t* src = &sm.v[voff[ch][t4] + ((cidx ^ vswz[ch][t4]) << 4)];
+          const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2*)(src));
+          a[2 * t4] = r[0];
+          a[2 * t4 + 1] = r[1];
+        }
+        oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
+      }
+      lacc = mfma_f8(ones, pw, lacc, kE8M0One, pscale);
+    }
+  }
+
+  // ---- epilogue
+  const float l_tot = lacc[0];
+  const int qi = q0w + col;
+  if (qi < S) {
+    const float inv = v_descale / l_tot;
+    __bf16* orow = o + ((int64_t)b * S * H + (int64_t)qi * H + h) * kDV;
+#pragma unroll
+    for (int d = 0; d < kDV / 32; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[d][g * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + d * 32 + g * 8 + half * 4) = w;
+      }
+    if (lse != nullptr && half == 0)
+      lse[(int64_t)bh * S + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  }
+}
+
+}  // namespace
+
+int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int S, int H, int d_qk, float softmax_scale, int causal, float q_descale,
+                    float k_descale, float v_descale, hipStream_t stream) {
+  const int nqb = (S + kBM - 1) / kBM;
+  const int BH = B * H;
+  const dim3 grid((unsigned)nqb * (unsigned)BH);
+  const float c_log2 = softmax_scale * q_descale * k_descale * 1.4426950408889634f;
+  // running-max refresh threshold (log2 units, 0..8); 0 = refresh on any increase
+  static const float lazy_log2 = [] {
+    const char* e = getenv("CPATTN_FP8_LAZY_LOG2");
+    float x = e ? strtof(e, nullptr) : 0.0f;
+    return (x >= 0.0f && x <= 8.0f) ? x : 0.0f;
+  }();
+  if (d_qk == 128)
+    hipLaunchKernelGGL(attn_fwd_fp8_kernel<128>, grid, dim3(kThreads), 0, stream,
+                       (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse,
+                       S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2);
+  else
+    hipLaunchKernelGGL(attn_fwd_fp8_kernel<192>, grid, dim3(kThreads), 0, stream,
+                       (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse,
+                       S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace cpattn

@@ -1,0 +1,73 @@
+"""The library's GPU amax and E4M3FN quantizer are bit-exact with the
+oracle's codec (integer/byte results: exact equality)."""
+import numpy as np
+import pytest
+import torch
+
+import causal_prefill_attention_attn_amd as pkg
+
+from gpu_util import DEV
+
+pytestmark = pytest.mark.gpu
+
+
+def _special_values(oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode_e4m3(codes)
+    vals = vals[np.isfinite(vals)]
+    pos = np.unique(np.abs(vals))
+    mids = (pos[1:] + pos[:-1]) / 2
+    extra = np.array([448.0, 449.0, 463.9, 464.0, 464.1, 479.0, 480.0, 1e4, 3e38, np.inf,
+                      2.0 ** -10, 2.0 ** -11, 1e-30, 1e-45, 0.0])
+    base = np.concatenate([pos, mids, extra]).astype(np.float32)
+    up = np.nextafter(base, np.float32(np.inf))
+    dn = np.nextafter(base, np.float32(0))
+    allv = np.concatenate([base, up, dn])
+    return np.concatenate([allv, -allv]).astype(np.float32)
+
+
+def test_quantize_special_values_bit_exact(oracle):
+    x = _special_values(oracle)
+    for descale in (1.0, 0.25, 3.0, 0.0123):
+        ref = oracle.quantize_e4m3(x, descale)
+        tx = torch.from_numpy(x).to(DEV)
+        out = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+        assert pkg.attn_quantize_e4m3(tx.data_ptr(), x.size, descale, out.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, [(float(x[i]), descale, hex(got[i]), hex(ref[i])) for i in bad[:10]]
+
+
+def test_quantize_nan_maps_to_0x7f(oracle):
+    x = np.array([np.nan, -np.nan], np.float32)
+    tx = torch.from_numpy(x).to(DEV)
+    out = torch.empty((2,), dtype=torch.uint8, device=DEV)
+    assert pkg.attn_quantize_e4m3(tx.data_ptr(), 2, 1.0, out.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert list(out.cpu().numpy()) == [0x7F, 0x7F] == list(oracle.quantize_e4m3(x, 1.0))
+
+
+@pytest.mark.parametrize("recipe_scale", [1.0, 37.5, 1e-3])
+def test_quantize_fp8_random_tensor(oracle, recipe_scale):
+    rng = np.random.default_rng(99)
+    x = (rng.standard_normal(3_000_001) * recipe_scale).astype(np.float32)
+    x[12345] = -7.5 * recipe_scale * 10
+    codes, descale = pkg.quantize_fp8(torch.from_numpy(x).to(DEV))
+    torch.cuda.synchronize()
+    assert np.float32(descale) == np.float32(oracle.descale_amax(x))
+    assert np.array_equal(codes.cpu().numpy(), oracle.quantize_e4m3(x, oracle.descale_amax(x)))
+
+
+def test_amax_zero_and_nan(oracle):
+    x = np.zeros(1000, np.float32)
+    codes, descale = pkg.quantize_fp8(torch.from_numpy(x).to(DEV))
+    assert descale == 1.0 and int(codes.sum()) == 0
+    x[17] = np.nan
+    x[500] = -3.0
+    out = torch.empty((1,), dtype=torch.float32, device=DEV)
+    tx = torch.from_numpy(x).to(DEV)
+    assert pkg.attn_amax_f32(tx.data_ptr(), x.size, out.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert float(out.item()) == 3.0
