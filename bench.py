@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one float32 elementwise copy of this many MiB before the "
+                         "warmup (reads and writes exactly that many bytes): the reference "
+                         "for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -115,6 +119,15 @@ def main():
     o = torch.empty((w.B, w.S, w.H, w.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("bench: calibration copy of %d MiB done" % args.calib_copy_mb)
+        del src, dst
 
     def step():
         pkg.flash_attn_func(t[0], t[1], t[2], softmax_scale=w.softmax_scale, causal=True,

@@ -16,12 +16,16 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcpattn.so")
 SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_fp8.hip", "quant.hip"]
+HEADERS = ["attn_device.h", "attn_kernels.h"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 ALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # scores and probabilities are never NaN for finite inputs; without this
+    # every fmaxf over matrix-core results gets a NaN-quieting instruction
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
 ]
 

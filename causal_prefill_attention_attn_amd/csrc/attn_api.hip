@@ -61,6 +61,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
       (lse && !aligned(lse, 4)))
     return ATTN_ERR_ALIGN;
   const int64_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 1;
+  // the kernels address one batch of q/k/v with 32-bit byte offsets (plus a
+  // tile of slack past the last row)
+  if ((S + 256) * H * d_qk * esz >= ((int64_t)1 << 32)) return ATTN_ERR_SHAPE;
   const int64_t rows = B * S * H;
   const int64_t nq = rows * d_qk * esz, nv = rows * d_v * esz, no = rows * d_v * 2;
   const int64_t nl = B * H * S * 4;

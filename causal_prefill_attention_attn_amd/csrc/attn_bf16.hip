@@ -19,67 +19,54 @@
 //                   rounding: no LDS round trip for P.  The O accumulator of
 //                   lane l belongs to query (l % 32) only, so the online
 //                   rescale and the final 1/l are per-lane scalars.
-// V^T needs keys contiguous per value column; the tile is transposed in
-// registers while it is staged into LDS, with the keys of each 16-key group
-// stored in the order the P^T operand enumerates them (bits 2 and 3 of the
-// key offset swapped), so each lane fetches its 8 keys with one 16-byte read.
+// V^T comes from a row-major V tile in LDS through ds_read_b64_tr_b16: 16
+// lanes supply four key rows of 16 values and each lane receives one value
+// column of those four keys.  Rows are stored with a 32-byte chunk swizzle
+// so that the eight 32-byte pieces one read instruction touches per 32
+// lanes fall in distinct banks.  K/V tiles are double-buffered in LDS with
+// global loads two tiles ahead, one workgroup barrier per tile.  The row
+// sum adds the probabilities in fp32 before their bf16 rounding.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_device.h"
 #include "attn_kernels.h"
 
 namespace cpattn {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kBM = 32 * kWaves;     // query rows per workgroup
-constexpr int kBN = 64;              // keys per tile
 constexpr int kDV = 128;             // value head dimension
 constexpr int kThreads = 64 * kWaves;
+constexpr int kVRow = kDV * 2;       // bytes per V row
 
-// v_permlane32_swap on two copies of x leaves {own value, value of lane l^32}
-// in its two results (which one is which depends on the lane half), so
-// combining both with a commutative operation gives the pair result in
-// every lane.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+// 32-byte chunk swizzle of a V row: the four consecutive keys one transposed
+// read covers land on four distinct even chunk slots
+__device__ __forceinline__ int v_swz(int key) { return (key & 3) << 1; }
 
-// position of key offset r (0..63) inside a Vt row: bits 2 and 3 swapped
-__device__ __forceinline__ int vt_pos(int r) {
-  return (r & ~12) | ((r >> 2) & 1) << 3 | ((r >> 3) & 1) << 2;
-}
-
-template <int DQK>
+template <int DQK, int BN>
 struct Smem {
-  static constexpr int kPitch = DQK + 8;   // bf16 elements per K row (+16 B breaks bank aliasing)
-  static constexpr int vPitch = kBN + 8;   // bf16 elements per V^T row
-  __bf16 k[kBN * kPitch];
-  __bf16 vt[kDV * vPitch];
+  static constexpr int kPitch = DQK * 2 + 16;  // bytes per K row (+16 B breaks bank aliasing)
+  uint8_t k[2][BN * kPitch];
+  uint8_t v[2][BN * kVRow];
 };
 
-template <int DQK>
+template <int DQK, int BN>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                      float* __restrict__ lse, int S, int H, int BH, int nqb, float c_log2,
                      int causal) {
-  constexpr int kSteps = DQK / 16;           // k-steps of the QK^T product
-  constexpr int kChunksPerRow = DQK / 8;     // 16-byte chunks per K row
-  constexpr int kKChunks = kBN * kChunksPerRow / kThreads;
-  static_assert(kBN * kChunksPerRow % kThreads == 0, "K tile split");
-  static_assert(kBN / 4 * kDV / 8 == kThreads, "V tile split: one 4x8 block per thread");
-  using SM = Smem<DQK>;
-  __shared__ SM sm;
+  constexpr int kSteps = DQK / 16;                 // k-steps of the QK^T product
+  constexpr int kNKB = BN / 32;                    // 32-key S blocks per tile
+  constexpr int kKRowChunks = DQK * 2 / 16;        // 16-byte chunks per K row
+  constexpr int kKChunks = BN * kKRowChunks / kThreads;
+  constexpr int kVChunks = BN * (kVRow / 16) / kThreads;
+  static_assert(BN * kKRowChunks % kThreads == 0 && BN * (kVRow / 16) % kThreads == 0, "split");
+  using SM = Smem<DQK, BN>;
+  __shared__ __attribute__((aligned(16))) SM sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -96,156 +83,166 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int h = bh % H;
   const int q0 = qb * kBM;
   const int q0w = q0 + wave * 32;
-  const int64_t rowStrideQK = (int64_t)H * DQK;
-  const int64_t rowStrideV = (int64_t)H * kDV;
-  const __bf16* qbh = q + ((int64_t)b * S * H + h) * DQK;
-  const __bf16* kbh = k + ((int64_t)b * S * H + h) * DQK;
-  const __bf16* vbh = v + ((int64_t)b * S * H + h) * kDV;
+  const uint32_t rsQK = (uint32_t)H * DQK * 2;  // bytes between rows
+  const uint32_t rsV = (uint32_t)H * kVRow;
+  const int64_t bstrQK = (int64_t)S * rsQK;
+  const int64_t bstrV = (int64_t)S * rsV;
+  const uint8_t* qb8 = reinterpret_cast<const uint8_t*>(q) + b * bstrQK;
+  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(k) + b * bstrQK;
+  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(v) + b * bstrV;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb8, (uint32_t)bstrQK);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb8, (uint32_t)bstrQK);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb8, (uint32_t)bstrV);
 
   // ---- Q^T operand, kept in registers for the whole key loop
   bf16x8 qreg[kSteps];
   {
-    const int qi = q0w + col;
-    #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      if (qi < S)
-        qreg[s] = *reinterpret_cast<const bf16x8*>(qbh + qi * rowStrideQK + s * 16 + half * 8);
-      else
-        qreg[s] = bf16x8{};
-    }
+    const uint32_t off = (uint32_t)(q0w + col) * rsQK + h * DQK * 2 + half * 16;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      qreg[s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, off + s * 32));
   }
 
-  const int nkt_all = (S + kBN - 1) / kBN;
-  const int nkt = causal ? min(nkt_all, (q0 + kBM - 1) / kBN + 1) : nkt_all;
+  const int nkt_all = (S + BN - 1) / BN;
+  const int nkt = causal ? min(nkt_all, (q0 + kBM - 1) / BN + 1) : nkt_all;
 
-  // ---- register staging of one K/V tile (prefetched one tile ahead)
-  uint4 kst[kKChunks];
-  uint4 vst[4];
-  const int va = tid >> 4;        // key group: keys 4*va .. 4*va+3
-  const int vc = tid & 15;        // value chunk: columns 8*vc .. 8*vc+7
+  // ---- register staging of one K/V tile
+  uint32_t koff[kKChunks], vofs[kVChunks];
+  int klds[kKChunks], vlds[kVChunks];
+#pragma unroll
+  for (int j = 0; j < kKChunks; ++j) {
+    const int c = tid + j * kThreads;
+    const int r = c / kKRowChunks, cc = c % kKRowChunks;
+    koff[j] = (uint32_t)r * rsQK + h * DQK * 2 + cc * 16;
+    klds[j] = r * SM::kPitch + cc * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < kVChunks; ++j) {
+    const int c = tid + j * kThreads;
+    const int r = c >> 4, cc = c & 15;  // 16-byte chunk cc of row r
+    vofs[j] = (uint32_t)r * rsV + h * kVRow + cc * 16;
+    vlds[j] = r * kVRow + (((cc >> 1) ^ v_swz(r)) << 5) + (cc & 1) * 16;
+  }
+  u32x4 kst[kKChunks], vst[kVChunks];
   auto load_tile = [&](int t) {
-    const int key0 = t * kBN;
-    #pragma unroll
-    for (int j = 0; j < kKChunks; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / kChunksPerRow, cc = c % kChunksPerRow;
-      const int key = key0 + r;
-      kst[j] = key < S ? *reinterpret_cast<const uint4*>(kbh + key * rowStrideQK + cc * 8)
-                       : make_uint4(0, 0, 0, 0);
-    }
-    #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key0 + va * 4 + r;
-      vst[r] = key < S ? *reinterpret_cast<const uint4*>(vbh + key * rowStrideV + vc * 8)
-                       : make_uint4(0, 0, 0, 0);
-    }
+    const uint32_t kb0 = (uint32_t)(t * BN) * rsQK, vb0 = (uint32_t)(t * BN) * rsV;
+#pragma unroll
+    for (int j = 0; j < kKChunks; ++j) kst[j] = buffer_load16(rk, kb0 + koff[j]);
+#pragma unroll
+    for (int j = 0; j < kVChunks; ++j) vst[j] = buffer_load16(rv, vb0 + vofs[j]);
   };
-  auto store_tile = [&]() {
-    #pragma unroll
-    for (int j = 0; j < kKChunks; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / kChunksPerRow, cc = c % kChunksPerRow;
-      *reinterpret_cast<uint4*>(&sm.k[r * SM::kPitch + cc * 8]) = kst[j];
-    }
-    // 4 keys x 8 columns -> 8 columns x 4 keys
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vst[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vst[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vst[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vst[3]);
-    const int pos = vt_pos(va * 4);
-    #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = j >> 1;
-      uint2 out;
-      if (j & 1) {
-        out.x = (w0[d] >> 16) | (w1[d] & 0xffff0000u);
-        out.y = (w2[d] >> 16) | (w3[d] & 0xffff0000u);
-      } else {
-        out.x = (w0[d] & 0xffffu) | (w1[d] << 16);
-        out.y = (w2[d] & 0xffffu) | (w3[d] << 16);
-      }
-      *reinterpret_cast<uint2*>(&sm.vt[(vc * 8 + j) * SM::vPitch + pos]) = out;
-    }
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kKChunks; ++j) lds_store16(&sm.k[buf][klds[j]], kst[j]);
+#pragma unroll
+    for (int j = 0; j < kVChunks; ++j) lds_store16(&sm.v[buf][vlds[j]], vst[j]);
   };
+
+  // V^T operand reads: lane j of a 16-lane group supplies row j/4 (one key)
+  // and bytes (j%4)*8 of the 32-byte chunk (d*2 + (lane/16)%2) of that row.
+  // Operand element e of lane half h is key u*16 + (e/4)*8 + h*4 + e%4, so
+  // read A covers keys u*16 + h*4 + 0..3 and read B the same plus 8.
+  const int gj = lane & 15;
+  const int vgrp = (lane >> 4) & 1;
+  const int vrow = half * 4 + (gj >> 2);            // key offset of read A inside 16 keys
+  const int vbyte = (gj & 3) * 8;
 
   f32x16 oacc[kDV / 32];
-  #pragma unroll
+#pragma unroll
   for (int i = 0; i < kDV / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY;  // running row max of c*s (log2 domain)
   float l_run = 0.f;        // this lane's partial row sum (its half of the keys)
 
-  if (nkt > 0) load_tile(0);
+  if (nkt > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  if (nkt > 1) load_tile(1);
+
   for (int t = 0; t < nkt; ++t) {
-    __syncthreads();  // everyone is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (t + 1 < nkt) load_tile(t + 1);
+    const int buf = t & 1;
+    const int key0 = t * BN;
+    if (!(causal && key0 > q0w + 31)) {  // else: tile entirely above this wave's diagonal
+      const uint8_t* kt = sm.k[buf];
+      const uint8_t* vt = sm.v[buf];
 
-    const int key0 = t * kBN;
-    if (causal && key0 > q0w + 31) continue;  // tile entirely above this wave's diagonal
-
-    // ---- S^T = K . Q^T for two 32-key blocks
-    f32x16 sacc[kBN / 32];
-    #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) {
-      sacc[kb] = f32x16{};
-      const __bf16* krow = &sm.k[(kb * 32 + col) * SM::kPitch + half * 8];
-      #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + s * 16);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[kb], 0, 0, 0);
+      // ---- S^T = K . Q^T
+      f32x16 sacc[kNKB];
+#pragma unroll
+      for (int kb = 0; kb < kNKB; ++kb) {
+        sacc[kb] = f32x16{};
+        const uint8_t* krow = kt + (kb * 32 + col) * SM::kPitch + half * 16;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, lds_load16(krow + s * 32)), qreg[s], sacc[kb], 0, 0, 0);
       }
-    }
 
-    // ---- mask (diagonal and ragged-tail tiles only), running max
-    const int qi = q0w + col;
-    const bool need_mask = (causal && key0 + kBN - 1 > q0w) || key0 + kBN > S;
-    if (need_mask) {
-      #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-        #pragma unroll
+      // ---- mask (diagonal and ragged-tail tiles only), running max
+      if ((causal && key0 + BN - 1 > q0w) || key0 + BN > S) {
+        const int lim = causal ? min(q0w + col, S - 1) : S - 1;  // last visible key
+#pragma unroll
+        for (int kb = 0; kb < kNKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            sacc[kb][i] = key > lim ? -INFINITY : sacc[kb][i];
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < kNKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      const float tmax = pair_max(mx) * c_log2;
+      if (__any(tmax > m_run)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < kDV / 32; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      }
+
+      // ---- P = exp2(c*s - m), bf16, laid out as the B operand of P.V
+      bf16x8 pb[BN / 16];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < kNKB; ++kb)
+#pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (key >= S || (causal && key > qi)) sacc[kb][i] = -INFINITY;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c_log2, -m_run));
+          psum += p;
+          pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
         }
-    }
-    float mx = -INFINITY;
-    #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb)
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx * c_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+      l_run += psum;
 
-    // ---- P = exp2(c*s - m), bf16, laid out as the B operand of P.V
-    bf16x8 pb[kBN / 16];
-    float psum = 0.f;
-    #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb)
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c_log2, -m_new));
-        psum += p;
-        pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
-      }
-    l_run = l_run * alpha + psum;
-    #pragma unroll
-    for (int d = 0; d < kDV / 32; ++d)
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-
-    // ---- O^T += V^T . P^T
-    #pragma unroll
-    for (int d = 0; d < kDV / 32; ++d) {
-      const __bf16* vrow = &sm.vt[(d * 32 + col) * SM::vPitch + half * 8];
-      #pragma unroll
-      for (int u = 0; u < kBN / 16; ++u) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + u * 16);
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], oacc[d], 0, 0, 0);
+      // ---- O^T += V^T . P^T
+#pragma unroll
+      for (int u = 0; u < BN / 16; ++u) {
+        const int keyA = u * 16 + vrow, keyB = keyA + 8;
+#pragma unroll
+        for (int d = 0; d < kDV / 32; ++d) {
+          const int c32 = d * 2 + vgrp;
+          const i16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vt + keyA * kVRow +
+                                                          ((c32 ^ v_swz(keyA)) << 5) + vbyte));
+          const i16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vt + keyB * kVRow +
+                                                          ((c32 ^ v_swz(keyB)) << 5) + vbyte));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], oacc[d], 0, 0, 0);
+        }
       }
     }
+
+    // ---- stage the next tile into the other buffer, then prefetch t+2
+    if (t + 1 < nkt) store_tile(buf ^ 1);
+    __syncthreads();
+    if (t + 2 < nkt) load_tile(t + 2);
   }
 
   // ---- epilogue: O / l -> bf16, lse = ln2 * (m + log2 l)
@@ -254,13 +251,12 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (qi < S) {
     const float inv = 1.0f / l_tot;
     __bf16* orow = o + ((int64_t)b * S * H + (int64_t)qi * H + h) * kDV;
-    #pragma unroll
+#pragma unroll
     for (int d = 0; d < kDV / 32; ++d)
-      #pragma unroll
+#pragma unroll
       for (int g = 0; g < 4; ++g) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 w;
-        #pragma unroll
+#pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[d][g * 4 + e] * inv);
         *reinterpret_cast<bf16x4*>(orow + d * 32 + g * 8 + half * 4) = w;
       }
@@ -279,11 +275,11 @@ int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float
   const dim3 grid((unsigned)nqb * (unsigned)BH);
   const float c_log2 = softmax_scale * 1.4426950408889634f;
   if (d_qk == 128)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 64>), grid, dim3(kThreads), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, S,
                        H, BH, nqb, c_log2, causal);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<192>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<192, 32>), grid, dim3(kThreads), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, S,
                        H, BH, nqb, c_log2, causal);
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -7,7 +7,7 @@
 // Work is organised per wave as 32 queries against the keys of a tile, the
 // unit the pages cost (same section).
 //
-// Per wave (32 query rows), per 128-key tile:
+// Per wave (32 query rows), per tile of BN keys (128 at d_qk 128, 64 at 192):
 //   S^T = K . Q^T   A = K rows (one key per lane column), B = Q^T (one query
 //                   per lane column), 32 bytes of the head dimension per
 //                   lane per step.  Lane l of the result holds query l%32 and
@@ -39,37 +39,26 @@
 // 2^lazy_log2 of m; the per-block exponent absorbs the excess, so results
 // stay correct but the top weight is no longer exact (larger error on
 // peaked rows).
+//
+// K/V tiles are double-buffered in LDS: global loads for tile t+2 are in
+// flight while tile t is computed, and tile t+1 is written to the other
+// buffer after the compute, so each tile costs one workgroup barrier.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
 
+#include "attn_device.h"
 #include "attn_kernels.h"
 
 namespace cpattn {
 
 namespace {
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;   // query rows per workgroup
-constexpr int kBN = 128;           // keys per tile (two 64-key scale blocks)
 constexpr int kDV = 128;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kE8M0One = 127;      // E8M0 encoding of 2^0
-
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int scale_a, int scale_b) {
   // operand formats 0/0 = E4M3 x E4M3; op_sel 0 = byte 0 of each scale VGPR
@@ -87,25 +76,30 @@ __device__ __forceinline__ int p_key(int h, int e) {
   return (e >> 4) * 32 + ((e & 15) >> 2) * 8 + h * 4 + (e & 3);
 }
 
-template <int DQK>
+template <int DQK, int BN>
 struct Smem {
   static constexpr int kPitch = DQK + 16;  // bytes per K row (+16 B breaks bank aliasing)
-  uint8_t k[kBN * kPitch];
-  uint8_t v[kBN * kDV];                    // row-major, chunk-swizzled
+  static constexpr int kKBytes = BN * kPitch;
+  static constexpr int kVBytes = BN * kDV;
+  uint8_t k[2][kKBytes];
+  uint8_t v[2][kVBytes];                   // row-major, chunk-swizzled
 };
 
-template <int DQK>
+template <int DQK, int BN>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                     const uint8_t* __restrict__ v, __bf16* __restrict__ o,
                     float* __restrict__ lse, int S, int H, int BH, int nqb, float c_log2,
                     float v_descale, int causal, float lazy_log2) {
   constexpr int kSteps = DQK / 64;                 // 32x32x64 steps of Q.K^T
+  constexpr int kNKB = BN / 32;                    // 32-key S blocks per tile
+  constexpr int kNCH = BN / 64;                    // 64-key scale blocks per tile
   constexpr int kKRowChunks = DQK / 16;            // 16-byte chunks per K row
-  constexpr int kKChunks = kBN * kKRowChunks / kThreads;
-  constexpr int kVChunks = kBN * (kDV / 16) / kThreads;
-  static_assert(kBN * kKRowChunks % kThreads == 0 && kBN * (kDV / 16) % kThreads == 0, "split");
-  using SM = Smem<DQK>;
+  constexpr int kKChunks = BN * kKRowChunks / kThreads;
+  constexpr int kVChunks = BN * (kDV / 16) / kThreads;
+  static_assert(BN * kKRowChunks % kThreads == 0 && BN * (kDV / 16) % kThreads == 0, "split");
+  static_assert(BN % 64 == 0, "tiles hold whole 64-key scale blocks");
+  using SM = Smem<DQK, BN>;
   __shared__ __attribute__((aligned(16))) SM sm;
 
   const int tid = threadIdx.x;
@@ -121,79 +115,70 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int h = bh % H;
   const int q0 = qb * kBM;
   const int q0w = q0 + wave * 32;
-  const int64_t rsQK = (int64_t)H * DQK;
-  const int64_t rsV = (int64_t)H * kDV;
-  const uint8_t* qbh = q + ((int64_t)b * S * H + h) * DQK;
-  const uint8_t* kbh = k + ((int64_t)b * S * H + h) * DQK;
-  const uint8_t* vbh = v + ((int64_t)b * S * H + h) * kDV;
+  const uint32_t rsQK = (uint32_t)H * DQK;  // bytes between consecutive rows
+  const uint32_t rsV = (uint32_t)H * kDV;
+  const int64_t bstrQK = (int64_t)S * rsQK;
+  const int64_t bstrV = (int64_t)S * rsV;
+  // one batch of q/k/v per buffer resource; rows >= S read as zero
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + b * bstrQK, (uint32_t)bstrQK);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + b * bstrQK, (uint32_t)bstrQK);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + b * bstrV, (uint32_t)bstrV);
 
   // ---- Q^T operand: lane (query col, half) holds d = s*64 + half*32 .. +31
   i32x8 qreg[kSteps];
   {
-    const int qi = q0w + col;
+    const uint32_t off = (uint32_t)(q0w + col) * rsQK + h * DQK + half * 32;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      if (qi < S) {
-        const uint4* p = reinterpret_cast<const uint4*>(qbh + qi * rsQK + s * 64 + half * 32);
-        const uint4 x0 = p[0], x1 = p[1];
-        qreg[s] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                        (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      } else {
-        qreg[s] = i32x8{};
-      }
+      const u32x4 lo = buffer_load16(rq, off + s * 64);
+      const u32x4 hi = buffer_load16(rq, off + s * 64 + 16);
+      qreg[s] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   }
 
-  const int nkt_all = (S + kBN - 1) / kBN;
-  const int nkt = causal ? min(nkt_all, (q0 + kBM - 1) / kBN + 1) : nkt_all;
+  const int nkt_all = (S + BN - 1) / BN;
+  const int nkt = causal ? min(nkt_all, (q0 + kBM - 1) / BN + 1) : nkt_all;
 
-  uint4 kst[kKChunks];
-  uint4 vst[kVChunks];
+  // ---- staging of one K/V tile through registers
+  uint32_t koff[kKChunks], vofs[kVChunks];
+  int klds[kKChunks], vlds[kVChunks];
+#pragma unroll
+  for (int j = 0; j < kKChunks; ++j) {
+    const int c = tid + j * kThreads;
+    const int r = c / kKRowChunks, cc = c % kKRowChunks;
+    koff[j] = (uint32_t)r * rsQK + h * DQK + cc * 16;
+    klds[j] = r * SM::kPitch + cc * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < kVChunks; ++j) {
+    const int c = tid + j * kThreads;
+    const int r = c >> 3, cc = c & 7;
+    vofs[j] = (uint32_t)r * rsV + h * kDV + cc * 16;
+    vlds[j] = r * kDV + ((cc ^ v_swz(r)) << 4);
+  }
+  u32x4 kst[kKChunks], vst[kVChunks];
   auto load_tile = [&](int t) {
-    const int key0 = t * kBN;
+    const uint32_t kb0 = (uint32_t)(t * BN) * rsQK, vb0 = (uint32_t)(t * BN) * rsV;
 #pragma unroll
-    for (int j = 0; j < kKChunks; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / kKRowChunks, cc = c % kKRowChunks;
-      const int key = key0 + r;
-      kst[j] = key < S ? *reinterpret_cast<const uint4*>(kbh + key * rsQK + cc * 16)
-                       : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < kKChunks; ++j) kst[j] = buffer_load16(rk, kb0 + koff[j]);
 #pragma unroll
-    for (int j = 0; j < kVChunks; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c >> 3, cc = c & 7;
-      const int key = key0 + r;
-      vst[j] = key < S ? *reinterpret_cast<const uint4*>(vbh + key * rsV + cc * 16)
-                       : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < kVChunks; ++j) vst[j] = buffer_load16(rv, vb0 + vofs[j]);
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < kKChunks; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / kKRowChunks, cc = c % kKRowChunks;
-      *reinterpret_cast<uint4*>(&sm.k[r * SM::kPitch + cc * 16]) = kst[j];
-    }
+    for (int j = 0; j < kKChunks; ++j) lds_store16(&sm.k[buf][klds[j]], kst[j]);
 #pragma unroll
-    for (int j = 0; j < kVChunks; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c >> 3, cc = c & 7;
-      *reinterpret_cast<uint4*>(&sm.v[r * kDV + ((cc ^ v_swz(r)) << 4)]) = vst[j];
-    }
+    for (int j = 0; j < kVChunks; ++j) lds_store16(&sm.v[buf][vlds[j]], vst[j]);
   };
 
-  // per-lane LDS byte offsets of the V^T operand reads (independent of the tile):
-  // lane i of a 16-lane group supplies row i/2 (a key) and byte half i%2 of a
-  // 16-byte dv chunk; the group's dv chunk is (db*2 + (lane/16)%2)
+  // per-lane LDS byte offsets of the V^T operand reads: lane i of a 16-lane
+  // group supplies row i/2 (a key) and byte half i%2 of the 16-byte dv chunk
+  // d*2 + dvhalf; voff holds the row base plus byte half, vswz the row swizzle
   const int gi = lane & 15;
   const int dvhalf = (lane >> 4) & 1;
-  // voff: row base + byte half; vswz: the row's chunk swizzle (the chunk
-  // index d*2 + dvhalf is applied per value block in the loop)
-  int voff[2][4];  // [64-key block][8-byte group of the operand]
-  int vswz[2][4];
+  int voff[kNCH][4], vswz[kNCH][4];
 #pragma unroll
-  for (int ch = 0; ch < 2; ++ch)
+  for (int ch = 0; ch < kNCH; ++ch)
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const int key = ch * 64 + p_key(half, t4 * 8 + (gi >> 1));
@@ -210,104 +195,108 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   f32x16 lacc = f32x16{};   // every entry of a column holds the same row sum
   float m_run = -INFINITY;  // max of c*s in use (log2 domain)
 
-  if (nkt > 0) load_tile(0);
+  if (nkt > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  if (nkt > 1) load_tile(1);
+
   for (int t = 0; t < nkt; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < nkt) load_tile(t + 1);
+    const int buf = t & 1;
+    const int key0 = t * BN;
+    if (!(causal && key0 > q0w + 31)) {  // else: tile entirely above this wave's diagonal
+      const uint8_t* kt = sm.k[buf];
+      const uint8_t* vt = sm.v[buf];
 
-    const int key0 = t * kBN;
-    if (causal && key0 > q0w + 31) continue;
-
-    // ---- S^T = K . Q^T, four 32-key blocks
-    f32x16 sacc[kBN / 32];
+      // ---- S^T = K . Q^T, 32-key blocks
+      f32x16 sacc[kNKB];
 #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) {
-      sacc[kb] = f32x16{};
-      const uint8_t* krow = &sm.k[(kb * 32 + col) * SM::kPitch + half * 32];
+      for (int kb = 0; kb < kNKB; ++kb) {
+        sacc[kb] = f32x16{};
+        const uint8_t* krow = kt + (kb * 32 + col) * SM::kPitch + half * 32;
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(krow + s * 64);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(krow + s * 64 + 16);
-        const i32x8 a = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                         (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sacc[kb] = mfma_f8(a, qreg[s], sacc[kb], kE8M0One, kE8M0One);
+        for (int s = 0; s < kSteps; ++s)
+          sacc[kb] = mfma_f8(lds_load32(krow + s * 64, 16), qreg[s], sacc[kb], kE8M0One, kE8M0One);
       }
-    }
 
-    // ---- mask on diagonal / ragged tiles
-    const int qi = q0w + col;
-    if ((causal && key0 + kBN - 1 > q0w) || key0 + kBN > S) {
+      // ---- mask on diagonal / ragged tiles
+      if ((causal && key0 + BN - 1 > q0w) || key0 + BN > S) {
+        const int lim = causal ? min(q0w + col, S - 1) : S - 1;  // last visible key
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
+        for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (key >= S || (causal && key > qi)) sacc[kb][i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            sacc[kb][i] = key > lim ? -INFINITY : sacc[kb][i];
+          }
+      }
+
+      // ---- block maxima (64 keys = two S blocks, both lane halves)
+      float bmax[kNCH];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int ch = 0; ch < kNCH; ++ch) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[2 * ch][i], sacc[2 * ch + 1][i]));
+        bmax[ch] = pair_max(mx) * c_log2;
+        tmax = fmaxf(tmax, bmax[ch]);
+      }
+      if (__any(tmax > m_run + lazy_log2)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+#pragma unroll
+        for (int d = 0; d < kDV / 32; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+        lacc[0] *= alpha;
+      }
+
+      // ---- per 64-key block: P = e4m3(2^(c*s - m + k)), then P.V and ones.P
+#pragma unroll
+      for (int ch = 0; ch < kNCH; ++ch) {
+        // k = 8 - ceil(block max - m) puts the block maximum in (2^7, 2^8];
+        // k >= 0 since block max - m <= lazy_log2 <= 8
+        const float kf = fminf(8.0f - __builtin_ceilf(bmax[ch] - m_run), 126.0f);
+        const float ofs = kf - m_run;
+        const int pscale = kE8M0One - (int)kf;
+        i32x8 pw;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int kb = 2 * ch + (w >> 2);
+          const int i0 = (w & 3) * 4;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 0], c_log2, ofs));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 1], c_log2, ofs));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 2], c_log2, ofs));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 3], c_log2, ofs));
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+          pw[w] = word;
         }
-    }
-
-    // ---- block maxima (64 keys = two S blocks, both lane halves)
-    float bmax[2];
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      float mx = -INFINITY;
+        for (int d = 0; d < kDV / 32; ++d) {
+          const int cidx = d * 2 + dvhalf;
+          i32x2 r[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[2 * ch][i], sacc[2 * ch + 1][i]));
-      bmax[ch] = pair_max(mx) * c_log2;
-    }
-    const float tmax = fmaxf(bmax[0], bmax[1]);
-    if (__any(tmax > m_run + lazy_log2)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < kDV / 32; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-      lacc[0] *= alpha;
-    }
-
-    // ---- P = e4m3(2^(c*s - m + k_blk)), scale 2^-k_blk in E8M0
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      // k = 8 - ceil(block max - m) puts the block maximum in (2^7, 2^8]
-      // (k >= 0 since block max - m <= lazy_log2 <= 8)
-      float kf = 8.0f - __builtin_ceilf(bmax[ch] - m_run);
-      kf = fminf(kf, 126.0f);
-      const float ofs = kf - m_run;
-      const int pscale = kE8M0One - (int)kf;
-      i32x8 pw;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int kb = 2 * ch + (w >> 2);
-        const int i0 = (w & 3) * 4;
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 0], c_log2, ofs));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 1], c_log2, ofs));
-        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 2], c_log2, ofs));
-        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 3], c_log2, ofs));
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-        pw[w] = word;
-      }
-      // ---- O^T += V^T . P^T over this 64-key block, and l += ones . P^T
-#pragma unroll
-      for (int d = 0; d < kDV / 32; ++d) {
-        const int cidx = d * 2 + dvhalf;
-        i32x8 a;
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-          const uint8_t* src = &sm.v[voff[ch][t4] + ((cidx ^ vswz[ch][t4]) << 4)];
-          const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2*)(src));
-          a[2 * t4] = r[0];
-          a[2 * t4 + 1] = r[1];
+          for (int t4 = 0; t4 < 4; ++t4)
+            r[t4] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(vt + voff[ch][t4] +
+                                                            ((cidx ^ vswz[ch][t4]) << 4)));
+          const i32x8 a = __builtin_shufflevector(
+              __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3),
+              __builtin_shufflevector(r[2], r[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
         }
-        oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
+        lacc = mfma_f8(ones, pw, lacc, kE8M0One, pscale);
       }
-      lacc = mfma_f8(ones, pw, lacc, kE8M0One, pscale);
     }
+
+    // ---- stage the next tile into the other buffer, then prefetch t+2
+    if (t + 1 < nkt) store_tile(buf ^ 1);
+    __syncthreads();
+    if (t + 2 < nkt) load_tile(t + 2);
   }
 
   // ---- epilogue
@@ -346,11 +335,11 @@ int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float*
     return (x >= 0.0f && x <= 8.0f) ? x : 0.0f;
   }();
   if (d_qk == 128)
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<128>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, 128>), grid, dim3(kThreads), 0, stream,
                        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse,
                        S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2);
   else
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<192>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, 64>), grid, dim3(kThreads), 0, stream,
                        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse,
                        S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2);
   return hipGetLastError() == hipSuccess ? 0 : -1;

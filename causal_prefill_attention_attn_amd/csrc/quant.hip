@@ -19,19 +19,20 @@ __global__ void zero_u32(uint32_t* p) { *p = 0u; }
 
 __global__ void __launch_bounds__(256) amax_kernel(const float* __restrict__ x, int64_t n,
                                                    uint32_t* __restrict__ out) {
-  float m = 0.f;
+  // magnitudes as bit patterns: non-negative floats order like unsigned
+  // integers, so the max is exact, order-free and needs no float compare;
+  // NaN patterns (above the infinity pattern) are skipped
+  uint32_t m = 0u;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    m = fmaxf(m, fabsf(x[i]));  // fmaxf drops NaN operands
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  __shared__ float wmax[4];
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t a = __float_as_uint(x[i]) & 0x7fffffffu;
+    m = max(m, a <= 0x7f800000u ? a : 0u);
+  }
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t wmax[4];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    // non-negative floats order like their bit patterns: max is exact and order-free
-    atomicMax(out, __float_as_uint(m));
-  }
+  if (threadIdx.x == 0) atomicMax(out, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
 }
 
 __device__ __forceinline__ uint8_t e4m3_from_f32(float x) {

@@ -40,11 +40,11 @@ extern "C" {
 /* status codes */
 #define ATTN_OK 0
 #define ATTN_ERR_NULL (-1)        /* a required pointer is NULL */
-#define ATTN_ERR_SHAPE (-2)       /* B, S or H < 1, or a size overflows */
+#define ATTN_ERR_SHAPE (-2)       /* B, S or H < 1, or a size exceeds the 32-bit limits */
 #define ATTN_ERR_DTYPE (-3)       /* dtype is not ATTN_DTYPE_BF16 / ATTN_DTYPE_FP8 */
 #define ATTN_ERR_UNSUPPORTED (-4) /* (d_qk, d_v) not in {(128,128), (192,128)}, or causal not 0/1 */
 #define ATTN_ERR_SCALE (-5)       /* softmax_scale or a descale not finite and > 0 */
-#define ATTN_ERR_ALIGN (-6)       /* a pointer is not 16-byte aligned */
+#define ATTN_ERR_ALIGN (-6)       /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
 #define ATTN_ERR_ALIAS (-7)       /* an output buffer overlaps an input or the other output */
 #define ATTN_ERR_LAUNCH (-8)      /* the HIP runtime rejected the kernel launch */
 
@@ -89,9 +89,12 @@ const char* attn_status_string(int status);
  *   q/k/v_descale  FP8 only: per-tensor dequantization factors, finite and
  *                  > 0 (ignored for BF16)
  *   stream         hipStream_t or NULL
- * Pointers must be 16-byte aligned; o and lse must not overlap q, k, v or
- * each other.  Repeated calls on the same inputs give bitwise identical o
- * and lse (no atomics, fixed reduction order).
+ * q, k, v, o must be 16-byte aligned and lse 4-byte aligned; o and lse must
+ * not overlap q, k, v or each other.  One batch of q/k (S*H*d_qk elements)
+ * must stay below 4 GiB (the kernels use 32-bit offsets within a batch);
+ * larger problems return ATTN_ERR_SHAPE.  Inputs holding NaN (or inf) give
+ * unspecified outputs.  Repeated calls on the same inputs give bitwise
+ * identical o and lse (no atomics, fixed reduction order).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
              int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale, int causal, int dtype,
