@@ -40,12 +40,29 @@
 // stay correct but the top weight is no longer exact (larger error on
 // peaked rows).
 //
+// Two ways to form P (template flag kLean):
+//   exact  p = exp2(c*s - m + k) on the transcendental unit, then
+//          v_cvt_pk_fp8_f32 (round to nearest even), two bytes per op.
+//   lean   no exponential: the e4m3 bit pattern of 2^y (y = c*s - m + k) is
+//          written directly as the integer round(8*(y + 7) - d): the integer
+//          part of y lands in the exponent field (bias 7) and 8*frac(y) in
+//          the three mantissa bits, i.e. 2^f is replaced by 1 + f.  That is
+//          one multiply-add and one integer conversion per probability
+//          (v_cvt_pk_u8_f32 rounds to nearest even and clamps to [0,255]),
+//          the lean-P technique of "Como o motor de atencao FP8 da Zyphra
+//          funciona" on the miraibroadcast.com page.  The shift d = 0.4567
+//          makes the approximation unbiased on average (mean of decoded
+//          value / 2^y over a uniform fractional part is 1), so the row sum
+//          and the LSE carry no systematic bias; the block maximum y = 8
+//          still maps exactly to 256 (byte 0x78).
+//
 // K/V tiles are double-buffered in LDS: global loads for tile t+2 are in
 // flight while tile t is computed, and tile t+1 is written to the other
 // buffer after the compute, so each tile costs one workgroup barrier.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "attn_device.h"
 #include "attn_kernels.h"
@@ -59,6 +76,7 @@ constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 constexpr int kDV = 128;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kE8M0One = 127;      // E8M0 encoding of 2^0
+constexpr float kLeanShift = 0.4567f;  // lean-P re-centring, in units of 1/8 octave
 
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int scale_a, int scale_b) {
   // operand formats 0/0 = E4M3 x E4M3; op_sel 0 = byte 0 of each scale VGPR
@@ -85,7 +103,7 @@ struct Smem {
   uint8_t v[2][kVBytes];                   // row-major, chunk-swizzled
 };
 
-template <int DQK, int BN>
+template <int DQK, int BN, bool kLean>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                     const uint8_t* __restrict__ v, __bf16* __restrict__ o,
@@ -260,20 +278,35 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
         // k = 8 - ceil(block max - m) puts the block maximum in (2^7, 2^8];
         // k >= 0 since block max - m <= lazy_log2 <= 8
         const float kf = fminf(8.0f - __builtin_ceilf(bmax[ch] - m_run), 126.0f);
-        const float ofs = kf - m_run;
         const int pscale = kE8M0One - (int)kf;
-        i32x8 pw;
+        i32x8 pw = __builtin_nondeterministic_value(pw);  // every byte is written below
+        if constexpr (kLean) {
+          const float c8 = 8.0f * c_log2;
+          const float ofs8 = 8.0f * (7.0f + kf - m_run) - kLeanShift;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int kb = 2 * ch + (w >> 2);
-          const int i0 = (w & 3) * 4;
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 0], c_log2, ofs));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 1], c_log2, ofs));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 2], c_log2, ofs));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 3], c_log2, ofs));
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-          pw[w] = word;
+          for (int w = 0; w < 8; ++w) {
+            const int kb = 2 * ch + (w >> 2);
+            const int i0 = (w & 3) * 4;
+            unsigned word = (unsigned)pw[w];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][i0 + e], c8, ofs8), e, word);
+            pw[w] = (int)word;
+          }
+        } else {
+          const float ofs = kf - m_run;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const int kb = 2 * ch + (w >> 2);
+            const int i0 = (w & 3) * 4;
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 0], c_log2, ofs));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 1], c_log2, ofs));
+            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 2], c_log2, ofs));
+            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 3], c_log2, ofs));
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+            pw[w] = word;
+          }
         }
 #pragma unroll
         for (int d = 0; d < kDV / 32; ++d) {
@@ -334,14 +367,23 @@ int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float*
     float x = e ? strtof(e, nullptr) : 0.0f;
     return (x >= 0.0f && x <= 8.0f) ? x : 0.0f;
   }();
-  if (d_qk == 128)
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, 128>), grid, dim3(kThreads), 0, stream,
-                       (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse,
-                       S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2);
-  else
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<192, 64>), grid, dim3(kThreads), 0, stream,
-                       (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse,
-                       S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2);
+  // probability form: "lean" (default) or "exact"
+  static const bool lean = [] {
+    const char* e = getenv("CPATTN_FP8_P");
+    return !(e && strcmp(e, "exact") == 0);
+  }();
+#define CPATTN_LAUNCH_FP8(DQK, BN, LEAN)                                                          \
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, BN, LEAN>), grid, dim3(kThreads), 0, stream,     \
+                     (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, S, \
+                     H, BH, nqb, c_log2, v_descale, causal, lazy_log2)
+  if (d_qk == 128) {
+    if (lean) CPATTN_LAUNCH_FP8(128, 128, true);
+    else CPATTN_LAUNCH_FP8(128, 128, false);
+  } else {
+    if (lean) CPATTN_LAUNCH_FP8(192, 64, true);
+    else CPATTN_LAUNCH_FP8(192, 64, false);
+  }
+#undef CPATTN_LAUNCH_FP8
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
