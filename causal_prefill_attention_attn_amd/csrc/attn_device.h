@@ -39,6 +39,17 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
+// 16 bytes per lane from buffer offset `off` straight into LDS: lane l's
+// data lands at lds_base + 16*l (lds_base must be the same in every lane);
+// offsets past the buffer end write zeros.  Kept in a __device__ function:
+// used directly inside a kernel template, the builtin stops the host pass
+// from emitting the kernel's launch stub.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                                  uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base,
+                                           16, (int)off, 0, 0, 0);
+}
+
 // 16-byte LDS accesses
 __device__ __forceinline__ u32x4 lds_load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

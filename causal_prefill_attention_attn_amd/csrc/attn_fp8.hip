@@ -56,9 +56,8 @@
 //          and the LSE carry no systematic bias; the block maximum y = 8
 //          still maps exactly to 256 (byte 0x78).
 //
-// K/V tiles are double-buffered in LDS: global loads for tile t+2 are in
-// flight while tile t is computed, and tile t+1 is written to the other
-// buffer after the compute, so each tile costs one workgroup barrier.
+// K/V tiles pass through three LDS stages filled directly by buffer-to-LDS
+// loads issued two phases ahead (rows past the end read as zero).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -71,10 +70,7 @@ namespace cpattn {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 constexpr int kDV = 128;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kE8M0One = 127;      // E8M0 encoding of 2^0
 constexpr float kLeanShift = 0.4567f;  // lean-P re-centring, in units of 1/8 octave
 
@@ -94,31 +90,64 @@ __device__ __forceinline__ int p_key(int h, int e) {
   return (e >> 4) * 32 + ((e & 15) >> 2) * 8 + h * 4 + (e & 3);
 }
 
+// wait until at most n vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS layout of one pipeline stage: K rows of kKPitch bytes whose 16-byte
+// chunks are XOR-swizzled (conflict-free 16-byte reads by 16 consecutive
+// keys), V rows of 128 bytes swizzled by v_swz.  Rows are filled by
+// buffer-to-LDS loads: each load instruction writes 64 lanes x 16 bytes to
+// consecutive LDS addresses, so a lane picks the global chunk that belongs
+// at its slot (padding slots read past the end of the buffer: zeros).
 template <int DQK, int BN>
-struct Smem {
-  static constexpr int kPitch = DQK + 16;  // bytes per K row (+16 B breaks bank aliasing)
-  static constexpr int kKBytes = BN * kPitch;
+struct Layout {
+  static constexpr int kKC = DQK == 128 ? 8 : 16;          // chunk slots per K row
+  static constexpr int kKPitch = kKC * 16;
+  static constexpr int kKBytes = BN * kKPitch;
   static constexpr int kVBytes = BN * kDV;
-  uint8_t k[2][kKBytes];
-  uint8_t v[2][kVBytes];                   // row-major, chunk-swizzled
+  static constexpr int kStages = 4;
+  __device__ static int k_swz(int row) { return DQK == 128 ? (row >> 1) & 7 : row & 15; }
 };
 
-template <int DQK, int BN, bool kLean>
-__global__ void __launch_bounds__(kThreads, 2)
+template <int DQK, int BN>
+struct Smem {
+  using L = Layout<DQK, BN>;
+  uint8_t k[L::kStages][L::kKBytes];
+  uint8_t v[L::kStages][L::kVBytes];
+};
+
+// One workgroup of 4*kOcc waves per compute unit (kOcc waves per SIMD),
+// each wave owning 32 query rows; the 32*4*kOcc rows of the workgroup share
+// every K/V tile in LDS, which keeps K/V re-reads from L2 low.  Each wave is
+// software-pipelined one tile deep: in iteration t it issues the matrix
+// instructions of S(t+1) = K(t+1).Q^T and then computes the probabilities of
+// tile t on the vector unit while those run, so its own matrix and vector
+// work overlap; the other wave of the SIMD fills the remaining gaps (the
+// overlap of matrix and vector work that "Como o motor de atencao FP8 da
+// Zyphra funciona" on the miraibroadcast.com page describes, obtained here
+// from instruction order inside each wave).  One workgroup barrier per tile.
+template <int DQK, int BN, bool kLean, int kOcc>
+__global__ void __launch_bounds__(256 * kOcc, 1)
 attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                     const uint8_t* __restrict__ v, __bf16* __restrict__ o,
                     float* __restrict__ lse, int S, int H, int BH, int nqb, float c_log2,
                     float v_descale, int causal, float lazy_log2) {
+  using LY = Layout<DQK, BN>;
+  constexpr int kWaves = 4 * kOcc;
+  constexpr int kBM = 32 * kWaves;                 // query rows per workgroup
   constexpr int kSteps = DQK / 64;                 // 32x32x64 steps of Q.K^T
-  constexpr int kNKB = BN / 32;                    // 32-key S blocks per tile
-  constexpr int kNCH = BN / 64;                    // 64-key scale blocks per tile
-  constexpr int kKRowChunks = DQK / 16;            // 16-byte chunks per K row
-  constexpr int kKChunks = BN * kKRowChunks / kThreads;
-  constexpr int kVChunks = BN * (kDV / 16) / kThreads;
-  static_assert(BN * kKRowChunks % kThreads == 0 && BN * (kDV / 16) % kThreads == 0, "split");
-  static_assert(BN % 64 == 0, "tiles hold whole 64-key scale blocks");
+  constexpr int kKRowsPerLoad = 1024 / LY::kKPitch;
+  constexpr int kKL = BN / kKRowsPerLoad;          // 1 KB loads of K per tile
+  constexpr int kVL = BN / 8;                      // 1 KB loads of V per tile
+  constexpr int kLoads = kKL + kVL;
+  static_assert(BN == 64, "one 64-key scale block per tile");
   using SM = Smem<DQK, BN>;
-  __shared__ __attribute__((aligned(16))) SM sm;
+  __shared__ __attribute__((aligned(1024))) SM sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -157,112 +186,114 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int nkt_all = (S + BN - 1) / BN;
   const int nkt = causal ? min(nkt_all, (q0 + kBM - 1) / BN + 1) : nkt_all;
 
-  // ---- staging of one K/V tile through registers
-  uint32_t koff[kKChunks], vofs[kVChunks];
-  int klds[kKChunks], vlds[kVChunks];
+  // ---- tile t (K and V) lives in LDS buffer t % kStages.  A tile is kLoads
+  // buffer-to-LDS loads of 1 KB (K first, then V); wave w issues loads
+  // w, w + kWaves, ..., the same number and kinds in every wave.
+  static_assert(kLoads % kWaves == 0 && kKL % kWaves == 0, "uniform load split");
+  constexpr int kMine = kLoads / kWaves;   // loads each wave issues per tile
+  uint32_t go[kMine];  // global offset inside the tile (0xfffffff0: padding, reads zeros)
+  int lo_[kMine];      // LDS offset inside the stage (K region, then V region)
 #pragma unroll
-  for (int j = 0; j < kKChunks; ++j) {
-    const int c = tid + j * kThreads;
-    const int r = c / kKRowChunks, cc = c % kKRowChunks;
-    koff[j] = (uint32_t)r * rsQK + h * DQK + cc * 16;
-    klds[j] = r * SM::kPitch + cc * 16;
+  for (int i = 0; i < kMine; ++i) {
+    const int j = wave + i * kWaves;
+    if (i * kWaves < kKL) {  // the same kind of load for every wave
+      const int row = j * kKRowsPerLoad + lane / LY::kKC;
+      const int lc = (lane % LY::kKC) ^ LY::k_swz(row);  // logical chunk held by this slot
+      go[i] = lc * 16 < DQK ? (uint32_t)row * rsQK + h * DQK + lc * 16 : 0xfffffff0u;
+      lo_[i] = j * 1024;
+    } else {
+      const int jv = j - kKL;
+      const int row = jv * 8 + lane / 8;
+      const int lc = (lane % 8) ^ v_swz(row);
+      go[i] = (uint32_t)row * rsV + h * kDV + lc * 16;
+      lo_[i] = jv * 1024;
+    }
   }
+  auto issue_tile = [&](int t) {
+    const int buf = t % LY::kStages;
+    const uint32_t kb = (uint32_t)(t * BN) * rsQK, vb = (uint32_t)(t * BN) * rsV;
 #pragma unroll
-  for (int j = 0; j < kVChunks; ++j) {
-    const int c = tid + j * kThreads;
-    const int r = c >> 3, cc = c & 7;
-    vofs[j] = (uint32_t)r * rsV + h * kDV + cc * 16;
-    vlds[j] = r * kDV + ((cc ^ v_swz(r)) << 4);
-  }
-  u32x4 kst[kKChunks], vst[kVChunks];
-  auto load_tile = [&](int t) {
-    const uint32_t kb0 = (uint32_t)(t * BN) * rsQK, vb0 = (uint32_t)(t * BN) * rsV;
-#pragma unroll
-    for (int j = 0; j < kKChunks; ++j) kst[j] = buffer_load16(rk, kb0 + koff[j]);
-#pragma unroll
-    for (int j = 0; j < kVChunks; ++j) vst[j] = buffer_load16(rv, vb0 + vofs[j]);
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kKChunks; ++j) lds_store16(&sm.k[buf][klds[j]], kst[j]);
-#pragma unroll
-    for (int j = 0; j < kVChunks; ++j) lds_store16(&sm.v[buf][vlds[j]], vst[j]);
+    for (int i = 0; i < kMine; ++i) {
+      if (i * kWaves < kKL)
+        buffer_load_lds16(rk, &sm.k[buf][lo_[i]], go[i] == 0xfffffff0u ? go[i] : kb + go[i]);
+      else
+        buffer_load_lds16(rv, &sm.v[buf][lo_[i]], vb + go[i]);
+    }
   };
 
-  // per-lane LDS byte offsets of the V^T operand reads: lane i of a 16-lane
-  // group supplies row i/2 (a key) and byte half i%2 of the 16-byte dv chunk
-  // d*2 + dvhalf; voff holds the row base plus byte half, vswz the row swizzle
+  // V^T operand reads: the key of operand byte group t4 is p_key(half, t4*8 +
+  // gi/2) = that of group 0 plus 16*t4, and its row swizzle (key bits 1 and
+  // 3) does not depend on t4, so one base address serves all four reads: the
+  // chunk (d*2 + dvhalf) ^ swz sits at byte (vbase ^ (d << 5)) + 2048*t4,
+  // with vbase = row*128 + (gi%2)*8 + dvhalf*16 + (swz/2)*32.
   const int gi = lane & 15;
   const int dvhalf = (lane >> 4) & 1;
-  int voff[kNCH][4], vswz[kNCH][4];
-#pragma unroll
-  for (int ch = 0; ch < kNCH; ++ch)
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const int key = ch * 64 + p_key(half, t4 * 8 + (gi >> 1));
-      voff[ch][t4] = key * kDV + (gi & 1) * 8;
-      vswz[ch][t4] = v_swz(key);
-    }
+  const int vkey0 = p_key(half, gi >> 1);
+  const int vbase = vkey0 * kDV + (gi & 1) * 8 + dvhalf * 16 + (v_swz(vkey0) >> 1) * 32;
+  // K operand reads: row kb*32 + col (its swizzle depends on col only) and
+  // logical chunk s*4 + half*2 + part; the swizzled chunk offset is
+  // kbase ^ ((s*4 + part) << 4) with kbase = row offset | ((half*2 ^ swz) << 4)
+  const int kbase = col * LY::kKPitch + (((half * 2) ^ LY::k_swz(col)) << 4);
 
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+
+  auto qk = [&](int t, f32x16* sa) {  // S^T of tile t = K(t) . Q^T, two 32-key blocks
+    const uint8_t* kt = sm.k[t % LY::kStages];
+    sa[0] = f32x16{};
+    sa[1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint8_t* kblk = kt + kb * 32 * LY::kKPitch;
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(kblk + (kbase ^ ((s * 4) << 4)));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(kblk + (kbase ^ ((s * 4 + 1) << 4)));
+        sa[kb] = mfma_f8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qreg[s], sa[kb],
+                         kE8M0One, kE8M0One);
+      }
+  };
+  auto active = [&](int t) { return t < nkt && !(causal && t * BN > q0w + 31); };
 
   f32x16 oacc[kDV / 32];
 #pragma unroll
   for (int i = 0; i < kDV / 32; ++i) oacc[i] = f32x16{};
   f32x16 lacc = f32x16{};   // every entry of a column holds the same row sum
   float m_run = -INFINITY;  // max of c*s in use (log2 domain)
+  f32x16 sa[2], sb[2];      // score buffers of consecutive tiles
 
-  if (nkt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  // ---- prologue: tiles 0..2 issued, 0 and 1 complete, S(0) started
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+    if (t < nkt) issue_tile(t);
+  if (nkt > 2) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
   __syncthreads();
-  if (nkt > 1) load_tile(1);
+  if (active(0)) qk(0, sa);
 
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    const int key0 = t * BN;
-    if (!(causal && key0 > q0w + 31)) {  // else: tile entirely above this wave's diagonal
-      const uint8_t* kt = sm.k[buf];
-      const uint8_t* vt = sm.v[buf];
-
-      // ---- S^T = K . Q^T, 32-key blocks
-      f32x16 sacc[kNKB];
-#pragma unroll
-      for (int kb = 0; kb < kNKB; ++kb) {
-        sacc[kb] = f32x16{};
-        const uint8_t* krow = kt + (kb * 32 + col) * SM::kPitch + half * 32;
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s)
-          sacc[kb] = mfma_f8(lds_load32(krow + s * 64, 16), qreg[s], sacc[kb], kE8M0One, kE8M0One);
-      }
-
-      // ---- mask on diagonal / ragged tiles
+  auto step = [&](int t, f32x16* scur, f32x16* snext) {
+    // tile t+3 goes to the buffer of tile t-1, finished before the last barrier
+    const bool more = t + 3 < nkt;
+    if (more) issue_tile(t + 3);
+    // S(t+1) on the matrix unit while the probabilities of tile t are computed
+    if (active(t + 1)) qk(t + 1, snext);
+    if (active(t)) {
+      const int key0 = t * BN;
       if ((causal && key0 + BN - 1 > q0w) || key0 + BN > S) {
-        const int lim = causal ? min(q0w + col, S - 1) : S - 1;  // last visible key
+        const int lim = (causal ? min(q0w + col, S - 1) : S - 1) - key0;  // last visible offset
 #pragma unroll
-        for (int kb = 0; kb < kNKB; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            sacc[kb][i] = key > lim ? -INFINITY : sacc[kb][i];
+            const int kofs = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            scur[kb][i] = kofs > lim ? -INFINITY : scur[kb][i];
           }
       }
-
-      // ---- block maxima (64 keys = two S blocks, both lane halves)
-      float bmax[kNCH];
-      float tmax = -INFINITY;
+      float mx = -INFINITY;
 #pragma unroll
-      for (int ch = 0; ch < kNCH; ++ch) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[2 * ch][i], sacc[2 * ch + 1][i]));
-        bmax[ch] = pair_max(mx) * c_log2;
-        tmax = fmaxf(tmax, bmax[ch]);
-      }
-      if (__any(tmax > m_run + lazy_log2)) {
-        const float m_new = fmaxf(m_run, tmax);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(scur[0][i], scur[1][i]));
+      const float bmax = pair_max(mx) * c_log2;
+      if (__any(bmax > m_run + lazy_log2)) {
+        const float m_new = fmaxf(m_run, bmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
 #pragma unroll
@@ -271,65 +302,63 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
           for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
         lacc[0] *= alpha;
       }
-
-      // ---- per 64-key block: P = e4m3(2^(c*s - m + k)), then P.V and ones.P
+      // P = e4m3(2^(c*s - m + k)); k = 8 - ceil(block max - m) puts the block
+      // maximum in (2^7, 2^8]; k >= 0 since block max - m <= lazy_log2 <= 8
+      const float kf = fminf(8.0f - __builtin_ceilf(bmax - m_run), 126.0f);
+      const int pscale = kE8M0One - (int)kf;
+      i32x8 pw = __builtin_nondeterministic_value(pw);  // every byte is written below
+      if constexpr (kLean) {
+        const float c8 = 8.0f * c_log2;
+        const float ofs8 = 8.0f * (7.0f + kf - m_run) - kLeanShift;
 #pragma unroll
-      for (int ch = 0; ch < kNCH; ++ch) {
-        // k = 8 - ceil(block max - m) puts the block maximum in (2^7, 2^8];
-        // k >= 0 since block max - m <= lazy_log2 <= 8
-        const float kf = fminf(8.0f - __builtin_ceilf(bmax[ch] - m_run), 126.0f);
-        const int pscale = kE8M0One - (int)kf;
-        i32x8 pw = __builtin_nondeterministic_value(pw);  // every byte is written below
-        if constexpr (kLean) {
-          const float c8 = 8.0f * c_log2;
-          const float ofs8 = 8.0f * (7.0f + kf - m_run) - kLeanShift;
+        for (int w = 0; w < 8; ++w) {
+          const int kb = w >> 2;
+          const int i0 = (w & 3) * 4;
+          unsigned word = (unsigned)pw[w];
 #pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const int kb = 2 * ch + (w >> 2);
-            const int i0 = (w & 3) * 4;
-            unsigned word = (unsigned)pw[w];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][i0 + e], c8, ofs8), e, word);
-            pw[w] = (int)word;
-          }
-        } else {
-          const float ofs = kf - m_run;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const int kb = 2 * ch + (w >> 2);
-            const int i0 = (w & 3) * 4;
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 0], c_log2, ofs));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 1], c_log2, ofs));
-            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 2], c_log2, ofs));
-            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + 3], c_log2, ofs));
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-            pw[w] = word;
-          }
+          for (int e = 0; e < 4; ++e)
+            word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(scur[kb][i0 + e], c8, ofs8), e, word);
+          pw[w] = (int)word;
         }
+      } else {
+        const float ofs = kf - m_run;
 #pragma unroll
-        for (int d = 0; d < kDV / 32; ++d) {
-          const int cidx = d * 2 + dvhalf;
-          i32x2 r[4];
-#pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4)
-            r[t4] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2*)(vt + voff[ch][t4] +
-                                                            ((cidx ^ vswz[ch][t4]) << 4)));
-          const i32x8 a = __builtin_shufflevector(
-              __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3),
-              __builtin_shufflevector(r[2], r[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
+        for (int w = 0; w < 8; ++w) {
+          const int kb = w >> 2;
+          const int i0 = (w & 3) * 4;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 0], c_log2, ofs));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 1], c_log2, ofs));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 2], c_log2, ofs));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 3], c_log2, ofs));
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+          pw[w] = word;
         }
-        lacc = mfma_f8(ones, pw, lacc, kE8M0One, pscale);
       }
+      // ---- O^T += V^T . P^T and l += ones . P^T
+      const uint8_t* vt = sm.v[t % LY::kStages];
+#pragma unroll
+      for (int d = 0; d < kDV / 32; ++d) {
+        i32x2 r[4];
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+          r[t4] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2*)(vt + t4 * 16 * kDV + (vbase ^ (d << 5))));
+        const i32x8 a = __builtin_shufflevector(
+            __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3),
+            __builtin_shufflevector(r[2], r[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
+      }
+      lacc = mfma_f8(ones, pw, lacc, kE8M0One, pscale);
     }
-
-    // ---- stage the next tile into the other buffer, then prefetch t+2
-    if (t + 1 < nkt) store_tile(buf ^ 1);
+    // tile t+2 must be complete for S(t+2) in the next iteration
+    if (more) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
     __syncthreads();
-    if (t + 2 < nkt) load_tile(t + 2);
+  };
+  // unrolled by two so that the two score buffers swap roles without copies
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < nkt) step(t + 1, sb, sa);
   }
 
   // ---- epilogue
@@ -357,7 +386,9 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
 int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                     int S, int H, int d_qk, float softmax_scale, int causal, float q_descale,
                     float k_descale, float v_descale, hipStream_t stream) {
-  const int nqb = (S + kBM - 1) / kBM;
+  const int occ = 2;                      // waves per SIMD (register budget)
+  const int bm = 128 * occ;               // query rows per workgroup
+  const int nqb = (S + bm - 1) / bm;
   const int BH = B * H;
   const dim3 grid((unsigned)nqb * (unsigned)BH);
   const float c_log2 = softmax_scale * q_descale * k_descale * 1.4426950408889634f;
@@ -372,16 +403,16 @@ int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float*
     const char* e = getenv("CPATTN_FP8_P");
     return !(e && strcmp(e, "exact") == 0);
   }();
-#define CPATTN_LAUNCH_FP8(DQK, BN, LEAN)                                                          \
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, BN, LEAN>), grid, dim3(kThreads), 0, stream,     \
-                     (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, S, \
+#define CPATTN_LAUNCH_FP8(DQK, BN, LEAN, OCC)                                                     \
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, BN, LEAN, OCC>), grid, dim3(256 * OCC), 0, stream, \
+                     (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, S,   \
                      H, BH, nqb, c_log2, v_descale, causal, lazy_log2)
   if (d_qk == 128) {
-    if (lean) CPATTN_LAUNCH_FP8(128, 128, true);
-    else CPATTN_LAUNCH_FP8(128, 128, false);
+    if (lean) CPATTN_LAUNCH_FP8(128, 64, true, 2);
+    else CPATTN_LAUNCH_FP8(128, 64, false, 2);
   } else {
-    if (lean) CPATTN_LAUNCH_FP8(192, 64, true);
-    else CPATTN_LAUNCH_FP8(192, 64, false);
+    if (lean) CPATTN_LAUNCH_FP8(192, 64, true, 2);
+    else CPATTN_LAUNCH_FP8(192, 64, false, 2);
   }
 #undef CPATTN_LAUNCH_FP8
   return hipGetLastError() == hipSuccess ? 0 : -1;
