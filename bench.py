@@ -69,6 +69,29 @@ def device_inputs(w, torch, pkg, synth):
     return t, ds, (qf, kf, vf)
 
 
+def profiled_traffic(w, dtname):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled
+    by a copy of known size) for this workload, from profiles/; None when no
+    summary exists or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_%s_d%d_%s.md" % (dtname, w.d_qk, w.name))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "kernel_source",
+                                                      "kernel_source_sha256"):
+            k, val = line.split(":", 1)
+            fields[k] = val.strip()
+    try:
+        src = open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()
+    except (KeyError, OSError):
+        return None
+    if hashlib.sha256(src).hexdigest() != fields.get("kernel_source_sha256"):
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(w, host, seconds, synth):
     """Time the fp64 oracle on a bounded sample of the same workload: a growing
     set of query rows of head 0, until about `seconds` of CPU work."""
@@ -178,7 +201,8 @@ def main():
                    "frac_of_peak": round(value / PEAK_TFLOPS[dtname], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS[dtname], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS[dtname], 4), "traffic": None,
+                     "frac": round(achieved / PEAK_TFLOPS[dtname], 4),
+                     "traffic": profiled_traffic(w, dtname),
                      "kernel": "attn_fwd_%s_kernel<%d>" % (dtname, w.d_qk),
                      "kernel_ms_mean": round(avg_kern, 4),
                      "compulsory_bytes": compulsory},
