@@ -23,11 +23,21 @@
 // lanes supply four key rows of 16 values and each lane receives one value
 // column of those four keys.  Rows are stored with a 32-byte chunk swizzle
 // so that the eight 32-byte pieces one read instruction touches per 32
-// lanes fall in distinct banks.  K/V tiles are double-buffered in LDS with
-// global loads two tiles ahead, one workgroup barrier per tile.  The row
-// sum adds the probabilities in fp32 before their bf16 rounding.
+// lanes fall in distinct banks; K rows with a 16-byte chunk swizzle so that
+// 16 consecutive keys read 16 distinct chunks.  The row sum adds the
+// bf16-rounded probabilities that enter P.V (v_dot2 of pairs against
+// (1, 1), fp32 accumulation).
+//
+// Schedule: eight waves per workgroup (two per SIMD) share every K/V tile
+// in LDS.  Tiles reach LDS through buffer-to-LDS loads issued three tiles
+// ahead into four stages (rows past the end read as zero), one workgroup
+// barrier per tile.  Each wave is software-pipelined one tile deep: it
+// issues the matrix instructions of S for tile t+1 before computing the
+// probabilities of tile t, so its own matrix and vector work overlap.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_device.h"
 #include "attn_kernels.h"
@@ -36,41 +46,65 @@ namespace cpattn {
 
 namespace {
 
-constexpr int kWaves = 4;            // waves per workgroup
+constexpr int kWaves = 8;            // waves per workgroup, two per SIMD
 constexpr int kBM = 32 * kWaves;     // query rows per workgroup
 constexpr int kDV = 128;             // value head dimension
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVRow = kDV * 2;       // bytes per V row
+constexpr int kAhead = 3;            // tiles loaded ahead of the current one
+constexpr int kStages = 4;
 
 // 32-byte chunk swizzle of a V row: the four consecutive keys one transposed
 // read covers land on four distinct even chunk slots
 __device__ __forceinline__ int v_swz(int key) { return (key & 3) << 1; }
 
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS stage of BN keys: K rows of kKPitch bytes (16-byte chunk c of key r
+// at slot c ^ (r & 15); for d_qk = 192 the row has 32 slots, 24 used), V
+// rows of 256 bytes (32-byte chunk c of key r at c ^ v_swz(r)).
 template <int DQK, int BN>
-struct Smem {
-  static constexpr int kPitch = DQK * 2 + 16;  // bytes per K row (+16 B breaks bank aliasing)
-  uint8_t k[2][BN * kPitch];
-  uint8_t v[2][BN * kVRow];
+struct Layout {
+  static constexpr int kKC = DQK == 128 ? 16 : 32;   // 16-byte slots per K row
+  static constexpr int kKPitch = kKC * 16;
+  static constexpr int kKBytes = BN * kKPitch;
+  static constexpr int kVBytes = BN * kVRow;
 };
 
 template <int DQK, int BN>
-__global__ void __launch_bounds__(kThreads, 2)
+struct Smem {
+  using L = Layout<DQK, BN>;
+  uint8_t k[kStages][L::kKBytes];
+  uint8_t v[kStages][L::kVBytes];
+};
+
+template <int DQK, int BN>
+__global__ void __launch_bounds__(kThreads, 1)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                      float* __restrict__ lse, int S, int H, int BH, int nqb, float c_log2,
                      int causal) {
+  using LY = Layout<DQK, BN>;
   constexpr int kSteps = DQK / 16;                 // k-steps of the QK^T product
   constexpr int kNKB = BN / 32;                    // 32-key S blocks per tile
-  constexpr int kKRowChunks = DQK * 2 / 16;        // 16-byte chunks per K row
-  constexpr int kKChunks = BN * kKRowChunks / kThreads;
-  constexpr int kVChunks = BN * (kVRow / 16) / kThreads;
-  static_assert(BN * kKRowChunks % kThreads == 0 && BN * (kVRow / 16) % kThreads == 0, "split");
+  constexpr int kKRowsPerLoad = 1024 / LY::kKPitch;
+  constexpr int kKL = BN / kKRowsPerLoad;          // 1 KB loads of K per tile
+  constexpr int kVL = BN / 4;                      // 1 KB loads of V per tile
+  constexpr int kLoads = kKL + kVL;
+  static_assert(kLoads % kWaves == 0 && kKL % kWaves == 0, "uniform load split");
+  constexpr int kMine = kLoads / kWaves;           // loads each wave issues per tile
   using SM = Smem<DQK, BN>;
-  __shared__ __attribute__((aligned(16))) SM sm;
+  __shared__ __attribute__((aligned(1024))) SM sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;  // query column / key row / value column inside a 32-block
   const int half = lane >> 5;
 
@@ -106,96 +140,117 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int nkt_all = (S + BN - 1) / BN;
   const int nkt = causal ? min(nkt_all, (q0 + kBM - 1) / BN + 1) : nkt_all;
 
-  // ---- register staging of one K/V tile
-  uint32_t koff[kKChunks], vofs[kVChunks];
-  int klds[kKChunks], vlds[kVChunks];
+  // ---- tile t lives in LDS stage t % kStages: kLoads buffer-to-LDS loads of
+  // 1 KB (K first, then V); wave w issues loads w, w + 8, ...
+  uint32_t go[kMine];  // global offset inside the tile (0xfffffff0: padding, reads zeros)
+  int lo_[kMine];      // LDS offset inside the stage (K region, then V region)
 #pragma unroll
-  for (int j = 0; j < kKChunks; ++j) {
-    const int c = tid + j * kThreads;
-    const int r = c / kKRowChunks, cc = c % kKRowChunks;
-    koff[j] = (uint32_t)r * rsQK + h * DQK * 2 + cc * 16;
-    klds[j] = r * SM::kPitch + cc * 16;
+  for (int i = 0; i < kMine; ++i) {
+    const int j = wave + i * kWaves;
+    if (i * kWaves < kKL) {  // the same kind of load for every wave
+      const int row = j * kKRowsPerLoad + lane / LY::kKC;
+      const int lc = (lane % LY::kKC) ^ (row & 15);  // logical chunk held by this slot
+      go[i] = lc * 16 < DQK * 2 ? (uint32_t)row * rsQK + h * DQK * 2 + lc * 16 : 0xfffffff0u;
+      lo_[i] = j * 1024;
+    } else {
+      const int jv = j - kKL;
+      const int row = jv * 4 + lane / 16;
+      const int sl = lane % 16;                              // 16-byte slot of the row
+      const int lc = (((sl >> 1) ^ v_swz(row)) << 1) | (sl & 1);  // logical 16-byte chunk
+      go[i] = (uint32_t)row * rsV + h * kVRow + lc * 16;
+      lo_[i] = jv * 1024;
+    }
   }
-#pragma unroll
-  for (int j = 0; j < kVChunks; ++j) {
-    const int c = tid + j * kThreads;
-    const int r = c >> 4, cc = c & 15;  // 16-byte chunk cc of row r
-    vofs[j] = (uint32_t)r * rsV + h * kVRow + cc * 16;
-    vlds[j] = r * kVRow + (((cc >> 1) ^ v_swz(r)) << 5) + (cc & 1) * 16;
-  }
-  u32x4 kst[kKChunks], vst[kVChunks];
-  auto load_tile = [&](int t) {
+  auto issue_tile = [&](int t) {
+    const int st = t % kStages;
     const uint32_t kb0 = (uint32_t)(t * BN) * rsQK, vb0 = (uint32_t)(t * BN) * rsV;
 #pragma unroll
-    for (int j = 0; j < kKChunks; ++j) kst[j] = buffer_load16(rk, kb0 + koff[j]);
-#pragma unroll
-    for (int j = 0; j < kVChunks; ++j) vst[j] = buffer_load16(rv, vb0 + vofs[j]);
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kKChunks; ++j) lds_store16(&sm.k[buf][klds[j]], kst[j]);
-#pragma unroll
-    for (int j = 0; j < kVChunks; ++j) lds_store16(&sm.v[buf][vlds[j]], vst[j]);
+    for (int i = 0; i < kMine; ++i) {
+      if (i * kWaves < kKL)
+        buffer_load_lds16(rk, &sm.k[st][lo_[i]], go[i] == 0xfffffff0u ? go[i] : kb0 + go[i]);
+      else
+        buffer_load_lds16(rv, &sm.v[st][lo_[i]], vb0 + go[i]);
+    }
   };
 
+  // K operand of S block kb, step s: key kb*32 + col, logical chunk 2s + half
+  // at slot (2s + half) ^ (col & 15) = (2s) ^ hs with hs = half ^ (col & 15)
+  const int kbase = col * LY::kKPitch + ((half ^ (col & 15)) << 4);
+  auto kread = [&](const uint8_t* kt, int kb, int s) {
+    return __builtin_bit_cast(
+        bf16x8, lds_load16(kt + kb * 32 * LY::kKPitch + (kbase ^ (s << 5))));
+  };
   // V^T operand reads: lane j of a 16-lane group supplies row j/4 (one key)
   // and bytes (j%4)*8 of the 32-byte chunk (d*2 + (lane/16)%2) of that row.
   // Operand element e of lane half h is key u*16 + (e/4)*8 + h*4 + e%4, so
-  // read A covers keys u*16 + h*4 + 0..3 and read B the same plus 8.
+  // read A covers keys u*16 + h*4 + 0..3 and read B the same plus 8.  The row
+  // swizzle depends on key & 3 = (j/4) & 3 only, so one per-lane base serves
+  // every (u, d): chunk d*2 + vgrp sits at (vbase ^ (d << 6)) and the keys
+  // of block u at +u*16 rows (+8 rows for read B).
   const int gj = lane & 15;
   const int vgrp = (lane >> 4) & 1;
-  const int vrow = half * 4 + (gj >> 2);            // key offset of read A inside 16 keys
-  const int vbyte = (gj & 3) * 8;
+  const int vrow = half * 4 + (gj >> 2);
+  const int vbase = vrow * kVRow + (gj & 3) * 8 + ((vgrp ^ v_swz(vrow)) << 5);
+
+  auto active = [&](int t) { return t < nkt && !(causal && t * BN > q0w + 31); };
 
   f32x16 oacc[kDV / 32];
 #pragma unroll
   for (int i = 0; i < kDV / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY;  // running row max of c*s (log2 domain)
   float l_run = 0.f;        // this lane's partial row sum (its half of the keys)
+  f32x16 sa[kNKB], sb[kNKB];  // score buffers of consecutive tiles
 
-  if (nkt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  if (nkt > 1) load_tile(1);
-
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    const int key0 = t * BN;
-    if (!(causal && key0 > q0w + 31)) {  // else: tile entirely above this wave's diagonal
-      const uint8_t* kt = sm.k[buf];
-      const uint8_t* vt = sm.v[buf];
-
-      // ---- S^T = K . Q^T
-      f32x16 sacc[kNKB];
+  auto qk = [&](int t, f32x16* sc) {
+    const uint8_t* kt = sm.k[t % kStages];
 #pragma unroll
-      for (int kb = 0; kb < kNKB; ++kb) {
-        sacc[kb] = f32x16{};
-        const uint8_t* krow = kt + (kb * 32 + col) * SM::kPitch + half * 16;
+    for (int kb = 0; kb < kNKB; ++kb) {
+      sc[kb] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, lds_load16(krow + s * 32)), qreg[s], sacc[kb], 0, 0, 0);
-      }
+      for (int s = 0; s < kSteps; ++s)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kt, kb, s), qreg[s], sc[kb], 0, 0, 0);
+    }
+  };
 
+  // ---- prologue: tiles 0..2 issued, 0 and 1 complete, S(0) started
+#pragma unroll
+  for (int t = 0; t < kAhead; ++t)
+    if (t < nkt) issue_tile(t);
+  if (nkt > 2) wait_vmcnt<kMine>();
+  else wait_vmcnt<0>();
+  barrier_nofence();
+  if (active(0)) qk(0, sa);
+
+  auto step = [&](int t, f32x16* scur, f32x16* snext) {
+    // tile t+3 goes to the stage of tile t-1, finished before the last barrier
+    if (t + kAhead < nkt) issue_tile(t + kAhead);
+    // S(t+1) on the matrix unit while the probabilities of tile t are formed
+    if (active(t + 1)) qk(t + 1, snext);
+    if (active(t)) {
+      const int key0 = t * BN;
       // ---- mask (diagonal and ragged-tail tiles only), running max
       if ((causal && key0 + BN - 1 > q0w) || key0 + BN > S) {
-        const int lim = causal ? min(q0w + col, S - 1) : S - 1;  // last visible key
+        // last visible key offset, less this lane half's 4-key shift, so the
+        // comparisons below are against compile-time constants
+        const int lim = (causal ? min(q0w + col, S - 1) : S - 1) - key0 - half * 4;
 #pragma unroll
         for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            sacc[kb][i] = key > lim ? -INFINITY : sacc[kb][i];
+            const int kofs = kb * 32 + (i >> 2) * 8 + (i & 3);
+            scur[kb][i] = kofs > lim ? -INFINITY : scur[kb][i];
           }
       }
-      float mx = -INFINITY;
+      // row max: two chains of three-input maxima
+      float ma = -INFINITY, mb = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      const float tmax = pair_max(mx) * c_log2;
+        for (int i = 0; i < 16; i += 4) {
+          ma = fmaxf(ma, fmaxf(scur[kb][i], scur[kb][i + 1]));
+          mb = fmaxf(mb, fmaxf(scur[kb][i + 2], scur[kb][i + 3]));
+        }
+      const float tmax = pair_max(fmaxf(ma, mb)) * c_log2;
       if (__any(tmax > m_run)) {
         const float m_new = fmaxf(m_run, tmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -206,43 +261,64 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
       }
-
-      // ---- P = exp2(c*s - m), bf16, laid out as the B operand of P.V
+      // ---- P = exp2(c*s - m), bf16, laid out as the B operand of P.V; the
+      // row sum adds the rounded probabilities, two per v_dot2 against (1, 1)
       bf16x8 pb[BN / 16];
-      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c_log2, -m_run));
-          psum += p;
-          pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
-        }
-      l_run += psum;
-
-      // ---- O^T += V^T . P^T
+        for (int i = 0; i < 16; ++i)
+          pb[kb * 2 + (i >> 3)][i & 7] =
+              (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i], c_log2, -m_run));
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      float psa = 0.f, psb = 0.f;
 #pragma unroll
       for (int u = 0; u < BN / 16; ++u) {
-        const int keyA = u * 16 + vrow, keyB = keyA + 8;
+        psa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 0, 1), one2, psa, false);
+        psb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 2, 3), one2, psb, false);
+        psa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 4, 5), one2, psa, false);
+        psb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 6, 7), one2, psb, false);
+      }
+      l_run += psa + psb;
+
+      // ---- O^T += V^T . P^T, V^T reads two operands ahead of their use
+      constexpr int kPV = (BN / 16) * (kDV / 32);
+      const uint32_t vt = lds_addr(sm.v[t % kStages]);
+      auto vread = [&](int m) {
+        const int u = m / (kDV / 32), d = m % (kDV / 32);
+        const uint32_t a = vt + u * 16 * kVRow + (vbase ^ (d << 6));
+        const i16x4 ra = ds_read_tr16<0>(a);
+        const i16x4 rb = ds_read_tr16<8 * kVRow>(a);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vop[kPV];
+      vop[0] = vread(0);
+      vop[1] = vread(1);
 #pragma unroll
-        for (int d = 0; d < kDV / 32; ++d) {
-          const int c32 = d * 2 + vgrp;
-          const i16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vt + keyA * kVRow +
-                                                          ((c32 ^ v_swz(keyA)) << 5) + vbyte));
-          const i16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vt + keyB * kVRow +
-                                                          ((c32 ^ v_swz(keyB)) << 5) + vbyte));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u], oacc[d], 0, 0, 0);
+      for (int m = 0; m < kPV; ++m) {
+        if (m + 2 < kPV) {
+          vop[m + 2] = vread(m + 2);
+          lds_wait_n<4>(vop[m]);
+        } else if (m + 1 < kPV) {
+          lds_wait_n<2>(vop[m]);
+        } else {
+          lds_wait_n<0>(vop[m]);
         }
+        const int u = m / (kDV / 32), d = m % (kDV / 32);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m], pb[u], oacc[d], 0, 0, 0);
       }
     }
-
-    // ---- stage the next tile into the other buffer, then prefetch t+2
-    if (t + 1 < nkt) store_tile(buf ^ 1);
-    __syncthreads();
-    if (t + 2 < nkt) load_tile(t + 2);
+    // tile t+2 complete for S(t+2) in the next step (tile t+3 may stay in
+    // flight)
+    static_assert(kAhead == 3, "wait counts assume three tiles ahead");
+    if (t + 3 < nkt) wait_vmcnt<kMine>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+  };
+  // unrolled by two so that the score buffers swap roles without copies
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < nkt) step(t + 1, sb, sa);
   }
 
   // ---- epilogue: O / l -> bf16, lse = ln2 * (m + log2 l)

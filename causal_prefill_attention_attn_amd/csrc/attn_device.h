@@ -12,9 +12,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // v_permlane32_swap on two copies of x leaves {own value, value of lane
 // l^32} in its two results (which one is which depends on the lane half),
@@ -50,19 +49,52 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
                                            16, (int)off, 0, 0, 0);
 }
 
-// 16-byte LDS accesses
+// ds_read_b64_tr_b16 issued as inline assembly.  The compiler builtin for
+// it carries no alias information, so the wait-count pass makes every such
+// read wait until all buffer-to-LDS loads in flight have landed, which
+// drains the K/V prefetch each tile.  As assembly the read waits for
+// nothing; its result must be ordered with lds_wait_n() before use.  Lanes
+// 4r..4r+3 of a 16-lane group supply the 16 values of row r (four rows) and
+// lane i receives value i of every row.  `addr` is an LDS byte address; OFF
+// a constant byte offset (< 65536).
+template <int OFF>
+__device__ __forceinline__ i16x4 ds_read_tr16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+// s_waitcnt lgkmcnt(N), tied to one operand register set so that its uses
+// cannot be scheduled above it.  LDS operations complete in order, so with
+// at most N of them (and any scalar loads) still in flight every older LDS
+// read has landed.
+template <int N>
+__device__ __forceinline__ void lds_wait_n(bf16x8& a) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
+}
+
+// Workgroup barrier without a memory fence: s_barrier, guarded only
+// against compiler reordering of memory accesses.  __syncthreads() adds a
+// workgroup release, and the compiler counts every buffer-to-LDS load in
+// flight as an LDS store that the release must wait for, so each barrier
+// would drain the whole K/V prefetch.  Here a wave that issued such loads
+// makes them visible by waiting for them itself (s_waitcnt vmcnt) before it
+// arrives; every LDS read is consumed (its lgkmcnt wait passed) before the
+// barrier after which its buffer is refilled.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16-byte LDS read
 __device__ __forceinline__ u32x4 lds_load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
-__device__ __forceinline__ void lds_store16(void* p, u32x4 v) {
-  *reinterpret_cast<u32x4*>(p) = v;
-}
-
-// 32-byte operand from two 16-byte LDS reads at p and p + second
-__device__ __forceinline__ i32x8 lds_load32(const uint8_t* p, int second) {
-  const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
-  const i32x4 hi = *reinterpret_cast<const i32x4*>(p + second);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 }  // namespace cpattn
