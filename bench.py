@@ -69,27 +69,54 @@ def device_inputs(w, torch, pkg, synth):
     return t, ds, (qf, kf, vf)
 
 
-def profiled_traffic(w, dtname):
-    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled
-    by a copy of known size) for this workload, from profiles/; None when no
-    summary exists or the kernel source changed since it was taken."""
+def profiled(w, dtname):
+    """Figures rocprofv3 measured for this workload's kernel, from profiles/:
+    HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known
+    size) and the sustained shader clock (GRBM_GUI_ACTIVE / duration).  Both
+    None when no summary exists or the kernel source changed since it was
+    taken."""
     import hashlib
+    import re
+    none = {"traffic": None, "sclk_mhz": None}
     path = os.path.join(ROOT, "profiles", "attn_fwd_%s_d%d_%s.md" % (dtname, w.d_qk, w.name))
     if not os.path.exists(path):
-        return None
+        return none
     fields = {}
     for line in open(path):
         if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "kernel_source",
                                                       "kernel_source_sha256"):
             k, val = line.split(":", 1)
             fields[k] = val.strip()
+        m = re.search(r"sustained clock .*: (\d+) MHz", line)
+        if m:
+            fields["sclk_mhz"] = m.group(1)
     try:
         src = open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()
     except (KeyError, OSError):
-        return None
+        return none
     if hashlib.sha256(src).hexdigest() != fields.get("kernel_source_sha256"):
-        return None
-    return int(fields["traffic_bytes_per_launch"])
+        return none
+    return {"traffic": int(fields["traffic_bytes_per_launch"]),
+            "sclk_mhz": int(fields["sclk_mhz"]) if "sclk_mhz" in fields else None}
+
+
+def input_stats(w, host, nrows=64):
+    """Logit spread and effective number of attended keys, 1 / sum_j p_ij^2,
+    over seeded sample rows of head 0 (fp32 host inputs; diagnostics of the
+    workload, not a parity check)."""
+    qf, kf, _ = host
+    rng = np.random.default_rng(777)
+    rows = np.sort(rng.choice(w.S, size=min(nrows, w.S), replace=False))
+    k0 = kf[0, :, 0, :].astype(np.float64)
+    std, neff = [], []
+    for i in rows:
+        s = (k0[: i + 1] @ qf[0, i, 0, :].astype(np.float64)) * w.softmax_scale
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        std.append(float(s.std()) if i > 0 else 0.0)
+        neff.append(float(1.0 / np.sum(p * p)))
+    return {"sample_rows": int(rows.size), "logit_std_median": round(float(np.median(std)), 3),
+            "n_eff_median": round(float(np.median(neff)), 2)}
 
 
 def cpu_baseline(w, host, seconds, synth):
@@ -108,6 +135,7 @@ def cpu_baseline(w, host, seconds, synth):
                for x, d in zip((qf, kf, vf), ds)]
     rng = np.random.default_rng(4242)
     n, spent, flops, nrows = 8, 0.0, 0.0, 0
+    full_flops = w.B * w.H * w.S * (w.S + 1) / 2.0 * (w.d_qk + w.d_v) * 2.0
     while spent < seconds:
         # each chunk draws distinct rows; chunks are capped at S rows and repeat
         # until the time budget is spent
@@ -120,7 +148,7 @@ def cpu_baseline(w, host, seconds, synth):
         nrows += rows.size
         n *= 2
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "full_run_estimate_s": round(spent * full_flops / flops, 1),
             "sample": "%d uniformly drawn query rows (chunks of at most S distinct rows) of head 0 (batch %d) of %s, causal, "
                       "fp64 oracle, %.1f s" % (nrows, w.B, w.name, spent)}
 
@@ -162,6 +190,7 @@ def main():
         step()
     torch.cuda.synchronize()
     log("bench: warmup done")
+    ref_o, ref_lse = o.clone(), lse.clone()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -173,6 +202,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [s.elapsed_time(e) for s, e in ev]
+    identical = bool(torch.equal(o.view(torch.int16), ref_o.view(torch.int16)) and
+                     torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)))
+    prof = profiled(w, dtname)
     ms_step = wall * 1e3 / args.steps
     flops = w.causal_flops
     value = flops / (ms_step * 1e-3) / 1e12
@@ -204,10 +236,18 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS[dtname], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS[dtname], 4),
-                     "traffic": profiled_traffic(w, dtname),
+                     "traffic": prof["traffic"],
                      "kernel": "attn_fwd_%s_kernel<%d>" % (dtname, w.d_qk),
                      "kernel_ms_mean": round(avg_kern, 4),
+                     "kernel_ms_p10_median_p90": [round(float(x), 4) for x in
+                                                  np.percentile(kern_ms, [10, 50, 90])],
+                     "sclk_mhz_profiled": prof["sclk_mhz"],
+                     "frac_clock_adjusted": (round(achieved / (PEAK_TFLOPS[dtname] *
+                                                               prof["sclk_mhz"] / 2400.0), 4)
+                                             if prof["sclk_mhz"] else None),
                      "compulsory_bytes": compulsory},
+        "bitwise_identical_launches": identical,
+        "inputs": input_stats(w, host),
     }
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a sample")

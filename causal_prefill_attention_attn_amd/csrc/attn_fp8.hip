@@ -7,7 +7,7 @@
 // Work is organised per wave as 32 queries against the keys of a tile, the
 // unit the pages cost (same section).
 //
-// Per wave (32 query rows), per tile of BN keys (128 at d_qk 128, 64 at 192):
+// Per wave (32 query rows), per tile of 64 keys:
 //   S^T = K . Q^T   A = K rows (one key per lane column), B = Q^T (one query
 //                   per lane column), 32 bytes of the head dimension per
 //                   lane per step.  Lane l of the result holds query l%32 and
@@ -56,8 +56,8 @@
 //          and the LSE carry no systematic bias; the block maximum y = 8
 //          still maps exactly to 256 (byte 0x78).
 //
-// K/V tiles pass through three LDS stages filled directly by buffer-to-LDS
-// loads issued two phases ahead (rows past the end read as zero).
+// K/V tiles pass through four LDS stages filled directly by buffer-to-LDS
+// loads issued three tiles ahead (rows past the end read as zero).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>

@@ -67,6 +67,9 @@ WORKLOADS = {
                     "FP8 e4m3 causal fwd, B=1 H=32 S=32768 d=128, N(0,1)"),
     "C2x": Workload("C2x", 6, BF16, 1, 32, 32768, 128, 128, "gaussian",
                     "BF16 causal fwd, B=1 H=32 S=32768 d=128, N(0,1)"),
+    # one GPU's share when C4's 32 heads are split over eight GPUs
+    "C4h4": Workload("C4h4", 7, FP8, 1, 4, 32768, 128, 128, "llm",
+                     "FP8 e4m3 causal fwd, B=1 H=4 S=32768 d=128, LLM-like (1/8 of C4's heads)"),
 }
 
 

@@ -271,3 +271,25 @@ def test_fp8_descales_are_applied(oracle):
     ob, lb = oracle.attention(*(_bf16(x) for x in vals), oracle.BF16, 0.3, True)
     np.testing.assert_allclose(o8, ob, rtol=1e-14, atol=1e-15)
     np.testing.assert_allclose(l8, lb, rtol=1e-14, atol=1e-15)
+
+
+def test_lse_merge_of_key_halves_is_causal_attention(oracle):
+    """Pins the shard merge used by the sequence-parallel test: the oracle's
+    own non-causal attention over the first key half and causal attention
+    over the second half, merged through their LSE, equal its causal
+    attention of the second-half rows over the whole sequence."""
+    from merge_util import merge
+    rng = np.random.default_rng(5150)
+    N, H, D = 40, 2, 16
+    q, k, v = (rng.standard_normal((1, 2 * N, H, D)).astype(np.float32) for _ in range(3))
+    qb, kb, vb = (to_bf16_bits(x) for x in (q, k, v))
+    tau = 0.3
+    q2 = np.ascontiguousarray(qb[:, N:])
+    oa, la = oracle.attention(q2, np.ascontiguousarray(kb[:, :N]), np.ascontiguousarray(vb[:, :N]),
+                              oracle.BF16, tau, False)
+    ob, lb = oracle.attention(q2, np.ascontiguousarray(kb[:, N:]), np.ascontiguousarray(vb[:, N:]),
+                              oracle.BF16, tau, True)
+    mo, ml = merge([(oa, la), (ob, lb)])
+    ro, rl = oracle.attention(qb, kb, vb, oracle.BF16, tau, True, rows=np.arange(N, 2 * N))
+    np.testing.assert_allclose(mo, ro, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ml, rl, rtol=1e-12, atol=1e-12)
