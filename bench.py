@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--hadamard", action="store_true",
+                    help="also time the Hadamard rotation of Q, K, V (fp32) and of O (bf16) "
+                         "at the workload's shape, the optional step before FP8 quantization")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one float32 elementwise copy of this many MiB before the "
                          "warmup (reads and writes exactly that many bytes): the reference "
@@ -153,6 +156,53 @@ def cpu_baseline(w, host, seconds, synth):
                       "fp64 oracle, %.1f s" % (nrows, w.B, w.name, spent)}
 
 
+def time_hadamard(w, host, pkg, torch, stream, attn_ms, reps=10):
+    """Cost of the optional Hadamard rotation, per tensor, as mean times of
+    HIP events on the launching stream: the plain per-tensor quantization
+    (amax pass + encode pass) of Q, K, V against the fused rotate+quantize
+    passes, and the standalone rotation of O (bf16) that undoes a rotated V.
+    Rates count one read of the input per pass and one write of the codes."""
+    dev = torch.device("cuda:0")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    st = stream.cuda_stream
+    res, extra = {}, 0.0
+    for name, x in zip("qkv", host):
+        t = torch.from_numpy(x).to(dev)
+        d = t.shape[-1]
+        rows, n = t.numel() // d, t.numel()
+        amax = torch.empty((1,), dtype=torch.float32, device=dev)
+        codes = torch.empty(t.shape, dtype=torch.uint8, device=dev)
+        plain = timed(lambda: (pkg.attn_amax_f32(t.data_ptr(), n, amax.data_ptr(), st),
+                               pkg.attn_quantize_e4m3(t.data_ptr(), n, 1.0, codes.data_ptr(), st)))
+        rot = timed(lambda: (pkg.attn_hadamard_amax_f32(t.data_ptr(), rows, d, amax.data_ptr(), st),
+                             pkg.attn_hadamard_quantize_e4m3(t.data_ptr(), rows, d, 1.0,
+                                                             codes.data_ptr(), st)))
+        gbs = (2 * 4 + 1) * n / (rot * 1e-3) / 1e9
+        res[name] = {"quantize_ms": round(plain, 4), "rotate_quantize_ms": round(rot, 4),
+                     "rotate_quantize_GB/s": round(gbs, 1)}
+        extra += rot - plain
+        del t, codes
+    o = torch.empty((w.B, w.S, w.H, w.d_v), dtype=torch.bfloat16, device=dev).normal_()
+    y = torch.empty_like(o)
+    orot = timed(lambda: pkg.hadamard(o, out=y))
+    res["o_rotate_ms"] = round(orot, 4)
+    res["o_rotate_GB/s"] = round(2 * o.numel() * 2 / (orot * 1e-3) / 1e9, 1)
+    res["added_ms"] = round(extra + orot, 4)
+    res["added_frac_of_attention"] = round((extra + orot) / attn_ms, 4)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -249,6 +299,8 @@ def main():
         "bitwise_identical_launches": identical,
         "inputs": input_stats(w, host),
     }
+    if args.hadamard:
+        out["hadamard"] = time_hadamard(w, host, pkg, torch, stream, avg_kern)
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, synth)

@@ -64,6 +64,14 @@ def load_library():
     lib.attn_amax_f32.argtypes = [vp, i64, vp, vp]
     lib.attn_quantize_e4m3.restype = i32
     lib.attn_quantize_e4m3.argtypes = [vp, i64, f32, vp, vp]
+    lib.attn_hadamard_f32.restype = i32
+    lib.attn_hadamard_f32.argtypes = [vp, i64, i32, vp, vp]
+    lib.attn_hadamard_bf16.restype = i32
+    lib.attn_hadamard_bf16.argtypes = [vp, i64, i32, vp, vp]
+    lib.attn_hadamard_amax_f32.restype = i32
+    lib.attn_hadamard_amax_f32.argtypes = [vp, i64, i32, vp, vp]
+    lib.attn_hadamard_quantize_e4m3.restype = i32
+    lib.attn_hadamard_quantize_e4m3.argtypes = [vp, i64, i32, f32, vp, vp]
     _lib = lib
     return lib
 
@@ -90,6 +98,22 @@ def attn_amax_f32(x, n, amax_out, stream=None) -> int:
 
 def attn_quantize_e4m3(x, n, descale, out, stream=None) -> int:
     return int(load_library().attn_quantize_e4m3(x, n, descale, out, stream))
+
+
+def attn_hadamard_f32(x, rows, d, y, stream=None) -> int:
+    return int(load_library().attn_hadamard_f32(x, rows, d, y, stream))
+
+
+def attn_hadamard_bf16(x, rows, d, y, stream=None) -> int:
+    return int(load_library().attn_hadamard_bf16(x, rows, d, y, stream))
+
+
+def attn_hadamard_amax_f32(x, rows, d, amax_out, stream=None) -> int:
+    return int(load_library().attn_hadamard_amax_f32(x, rows, d, amax_out, stream))
+
+
+def attn_hadamard_quantize_e4m3(x, rows, d, descale, out, stream=None) -> int:
+    return int(load_library().attn_hadamard_quantize_e4m3(x, rows, d, descale, out, stream))
 
 
 # ------------------------------------------------------------ torch helpers
@@ -155,20 +179,55 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_d
     return out, lse
 
 
-def quantize_fp8(x):
+def quantize_fp8(x, rotate=False):
     """Per-tensor E4M3FN quantization on the GPU: returns (codes uint8, descale)
-    with descale = amax / 448 computed in fp32 (1.0 for an all-zero tensor)."""
+    with descale = amax / 448 computed in fp32 (1.0 for an all-zero tensor).
+    With ``rotate`` the rows of the last dimension (128 or 192) are rotated by
+    the Hadamard matrix H first (as ``hadamard``), inside the quantization
+    passes: the codes are those of x . H."""
     torch = _torch()
     import numpy as np
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous float32 CUDA tensor")
     n = x.numel()
+    st = _stream_handle(x.device)
     amax = torch.empty((1,), dtype=torch.float32, device=x.device)
-    _check(attn_amax_f32(x.data_ptr(), n, amax.data_ptr(), _stream_handle(x.device)),
-           "attn_amax_f32")
+    if rotate:
+        d = x.shape[-1]
+        _check(attn_hadamard_amax_f32(x.data_ptr(), n // d, d, amax.data_ptr(), st),
+               "attn_hadamard_amax_f32")
+    else:
+        _check(attn_amax_f32(x.data_ptr(), n, amax.data_ptr(), st), "attn_amax_f32")
     a = np.float32(amax.item())
     descale = float(a / np.float32(448.0)) if a > 0 else 1.0
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    _check(attn_quantize_e4m3(x.data_ptr(), n, descale, codes.data_ptr(),
-                              _stream_handle(x.device)), "attn_quantize_e4m3")
+    if rotate:
+        _check(attn_hadamard_quantize_e4m3(x.data_ptr(), n // d, d, descale, codes.data_ptr(), st),
+               "attn_hadamard_quantize_e4m3")
+    else:
+        _check(attn_quantize_e4m3(x.data_ptr(), n, descale, codes.data_ptr(), st),
+               "attn_quantize_e4m3")
     return codes, descale
+
+
+def hadamard(x, out=None):
+    """Rotate the last dimension (128 or 192) of a contiguous float32 or
+    bfloat16 CUDA tensor by the normalized block Walsh-Hadamard matrix H:
+    returns x . H (``out`` may be ``x`` for an in-place rotation).  H is its
+    own inverse, so ``hadamard(hadamard(x))`` restores x up to rounding; the
+    attention output of Q.H, K.H, V.H rotated once more is the attention of
+    Q, K, V."""
+    torch = _torch()
+    if not x.is_cuda or not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be a contiguous CUDA tensor")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
+    d = x.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must match x in shape, dtype and layout")
+    fn = attn_hadamard_f32 if x.dtype == torch.float32 else attn_hadamard_bf16
+    _check(fn(x.data_ptr(), x.numel() // d, d, out.data_ptr(), _stream_handle(x.device)),
+           "attn_hadamard")
+    return out

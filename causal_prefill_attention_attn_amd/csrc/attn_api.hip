@@ -105,3 +105,60 @@ int attn_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out, v
 }
 
 }  // extern "C"
+
+namespace {
+
+int hadamard(const void* x, int64_t rows, int d, void* y, int esz, void* stream) {
+  if (!x || !y) return ATTN_ERR_NULL;
+  if (rows < 1) return ATTN_ERR_SHAPE;
+  if (d != 128 && d != 192) return ATTN_ERR_UNSUPPORTED;
+  if (rows > INT64_MAX / ((int64_t)d * esz)) return ATTN_ERR_SHAPE;
+  if (!aligned(x, esz) || !aligned(y, esz)) return ATTN_ERR_ALIGN;
+  const int64_t n = rows * d * esz;
+  if (x != y && overlap(x, n, y, n)) return ATTN_ERR_ALIAS;
+  return cpattn::launch_hadamard(x, rows, d, esz == 2, y, reinterpret_cast<hipStream_t>(stream)) == 0
+             ? ATTN_OK
+             : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_hadamard_f32(const float* x, int64_t rows, int d, float* y, void* stream) {
+  return hadamard(x, rows, d, y, 4, stream);
+}
+
+int attn_hadamard_bf16(const void* x, int64_t rows, int d, void* y, void* stream) {
+  return hadamard(x, rows, d, y, 2, stream);
+}
+
+int attn_hadamard_amax_f32(const float* x, int64_t rows, int d, float* amax_out, void* stream) {
+  if (!x || !amax_out) return ATTN_ERR_NULL;
+  if (rows < 1) return ATTN_ERR_SHAPE;
+  if (d != 128 && d != 192) return ATTN_ERR_UNSUPPORTED;
+  if (rows > INT64_MAX / ((int64_t)d * 4)) return ATTN_ERR_SHAPE;
+  if (!aligned(x, 4) || !aligned(amax_out, 4)) return ATTN_ERR_ALIGN;
+  if (overlap(amax_out, 4, x, rows * d * 4)) return ATTN_ERR_ALIAS;
+  return cpattn::launch_hadamard_amax(x, rows, d, amax_out,
+                                      reinterpret_cast<hipStream_t>(stream)) == 0
+             ? ATTN_OK
+             : ATTN_ERR_LAUNCH;
+}
+
+int attn_hadamard_quantize_e4m3(const float* x, int64_t rows, int d, float descale, uint8_t* out,
+                                void* stream) {
+  if (!x || !out) return ATTN_ERR_NULL;
+  if (rows < 1) return ATTN_ERR_SHAPE;
+  if (d != 128 && d != 192) return ATTN_ERR_UNSUPPORTED;
+  if (rows > INT64_MAX / ((int64_t)d * 4)) return ATTN_ERR_SHAPE;
+  if (!finite_positive(descale)) return ATTN_ERR_SCALE;
+  if (!aligned(x, 4)) return ATTN_ERR_ALIGN;
+  if (overlap(out, rows * d, x, rows * d * 4)) return ATTN_ERR_ALIAS;
+  return cpattn::launch_hadamard_quantize(x, rows, d, descale, out,
+                                          reinterpret_cast<hipStream_t>(stream)) == 0
+             ? ATTN_OK
+             : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -20,4 +20,13 @@ int launch_amax_f32(const float* x, int64_t n, float* amax_out, hipStream_t stre
 int launch_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out,
                          hipStream_t stream);
 
+// y[r] = x[r] . H for rows of d in {128, 192} elements (fp32, or bf16 when
+// bf16 is set); y may equal x.
+int launch_hadamard(const void* x, int64_t rows, int d, bool bf16, void* y, hipStream_t stream);
+// amax of the rotated fp32 rows; e4m3 codes of the rotated rows / descale
+int launch_hadamard_amax(const float* x, int64_t rows, int d, float* amax_out,
+                         hipStream_t stream);
+int launch_hadamard_quantize(const float* x, int64_t rows, int d, float descale, uint8_t* out,
+                             hipStream_t stream);
+
 }  // namespace cpattn

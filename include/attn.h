@@ -124,6 +124,47 @@ int attn_amax_f32(const float* x, int64_t n, float* amax_out, void* stream);
  */
 int attn_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out, void* stream);
 
+/*
+ * attn_hadamard_f32 / attn_hadamard_bf16 -- y[r,:] = x[r,:] . H for `rows`
+ * rows of d elements, with H the normalized Sylvester-Hadamard matrix of
+ * order 128 (d = 128) or block-diagonal with three order-64 blocks
+ * (d = 192).  H is symmetric and orthogonal: applying it twice restores x
+ * (up to rounding), and rotating Q and K by the same H leaves Q.K^T, hence
+ * the attention weights, unchanged.  Rotating Q, K and V before FP8
+ * quantization spreads outlier channels over the row and shrinks the
+ * quantization error, the largest part of the FP8 error ("Precisao,
+ * estabilidade e efeito na pratica" on the miraibroadcast.com page); the
+ * attention output of a rotated V is rotated back by applying H to O.
+ *   x     device, rows*d values (float32, or bfloat16 for _bf16), row-major
+ *   rows  >= 1
+ *   d     128 or 192 (else ATTN_ERR_UNSUPPORTED)
+ *   y     device, rows*d values (written); may be x itself (in place) but
+ *         must not overlap it otherwise (ATTN_ERR_ALIAS)
+ * Arithmetic is fp32; the bf16 variant rounds its result to nearest even.
+ * x and y must be 4-byte (f32) / 2-byte (bf16) aligned.
+ */
+int attn_hadamard_f32(const float* x, int64_t rows, int d, float* y, void* stream);
+int attn_hadamard_bf16(const void* x, int64_t rows, int d, void* y, void* stream);
+
+/*
+ * attn_hadamard_amax_f32 / attn_hadamard_quantize_e4m3 -- the per-tensor
+ * quantization of attn_amax_f32 / attn_quantize_e4m3 applied to the rotated
+ * rows x[r,:] . H (H as for attn_hadamard_f32) without writing the rotated
+ * tensor: one pass finds the largest rotated magnitude, a second rotates
+ * again and encodes, so the rotation adds no memory traffic to the
+ * quantization.  Both passes evaluate the rotation identically.
+ *   x         device, rows*d float32 values, row-major
+ *   rows, d   as for attn_hadamard_f32
+ *   amax_out  device, one float32 (written): max |(x . H)[i]|, NaN ignored
+ *   descale   finite and > 0
+ *   out       device, rows*d bytes (written): E4M3FN((x . H)[i] / descale),
+ *             rounding and saturation as attn_quantize_e4m3; must not
+ *             overlap x
+ */
+int attn_hadamard_amax_f32(const float* x, int64_t rows, int d, float* amax_out, void* stream);
+int attn_hadamard_quantize_e4m3(const float* x, int64_t rows, int d, float descale, uint8_t* out,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

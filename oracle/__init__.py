@@ -5,10 +5,12 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 (``causal_prefill_attention_attn_amd``) never imports it and shares no code
 with it.
 
-The arithmetic lives in ``attn_oracle.c`` (plain C, binary64, OpenMP over
-query rows); this module only builds that file with gcc and marshals numpy
-arrays through ctypes.  See the header of ``attn_oracle.c`` for the
-definition it computes and the passages of the pages it follows.
+The attention arithmetic lives in ``attn_oracle.c`` (plain C, binary64,
+OpenMP over query rows); this module builds that file with gcc and marshals
+numpy arrays through ctypes.  See the header of ``attn_oracle.c`` for the
+definition it computes and the passages of the pages it follows.  The one
+exception is the Hadamard rotation that may precede FP8 quantization
+(``hadamard``), a plain fp64 matrix product per block written here in numpy.
 """
 from __future__ import annotations
 
@@ -130,3 +132,34 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: int, tau: floa
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def hadamard_matrix(n: int) -> np.ndarray:
+    """Normalized Sylvester-Hadamard matrix of order n (a power of two), fp64:
+    H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]], scaled by 1/sqrt(n).  The
+    rotation of Q, K and V before FP8 quantization ("Precisao, estabilidade
+    e efeito na pratica" on the miraibroadcast.com page) uses this matrix;
+    the pages name the transform but not its order or normalization, so the
+    plainest orthogonal reading is taken."""
+    assert n >= 1 and n & (n - 1) == 0
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h / np.sqrt(n)
+
+
+def hadamard_block(d: int) -> int:
+    """Block order of the row rotation: 128 for rows of 128, 64 for 192."""
+    return {128: 128, 192: 64}[d]
+
+
+def hadamard(x: np.ndarray) -> np.ndarray:
+    """x . H over the last dimension d in {128, 192}, in fp64, with H
+    block-diagonal of normalized Sylvester-Hadamard blocks (one of 128, or
+    three of 64): a plain matrix product per block."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    n = hadamard_block(d)
+    h = hadamard_matrix(n)
+    blocks = x.reshape(x.shape[:-1] + (d // n, n))
+    return (blocks @ h).reshape(x.shape)

@@ -33,7 +33,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["attn_version", "attn_status_string", "attn_fwd", "attn_amax_f32",
-                            "attn_quantize_e4m3"]), names
+                            "attn_quantize_e4m3", "attn_hadamard_f32", "attn_hadamard_bf16",
+                            "attn_hadamard_amax_f32", "attn_hadamard_quantize_e4m3"]), names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -93,3 +94,24 @@ def test_quant_entry_points_reject(lib):
     assert pkg.attn_quantize_e4m3(Q, 10, 1.0, None) == -1
     assert pkg.attn_quantize_e4m3(Q, 0, 1.0, O) == -2
     assert pkg.attn_quantize_e4m3(Q, 16, 1.0, Q + 8) == -7
+
+
+def test_hadamard_entry_points_reject(lib):
+    for fn, esz in ((pkg.attn_hadamard_f32, 4), (pkg.attn_hadamard_bf16, 2)):
+        assert fn(None, 4, 128, O) == -1
+        assert fn(Q, 4, 128, None) == -1
+        assert fn(Q, 0, 128, O) == -2
+        assert fn(Q, 1 << 60, 128, O) == -2
+        assert fn(Q, 4, 64, O) == -4
+        assert fn(Q, 4, 256, O) == -4
+        assert fn(Q + 1, 4, 128, O) == -6
+        assert fn(Q, 4, 128, Q + 2 * esz) == -7     # partial overlap
+    assert pkg.attn_hadamard_amax_f32(None, 4, 128, O) == -1
+    assert pkg.attn_hadamard_amax_f32(Q, 0, 128, O) == -2
+    assert pkg.attn_hadamard_amax_f32(Q, 4, 64, O) == -4
+    assert pkg.attn_hadamard_amax_f32(Q, 4, 128, Q + 8) == -7
+    assert pkg.attn_hadamard_quantize_e4m3(Q, 4, 128, 1.0, None) == -1
+    assert pkg.attn_hadamard_quantize_e4m3(Q, 4, 192, 0.0, O) == -5
+    assert pkg.attn_hadamard_quantize_e4m3(Q, 4, 100, 1.0, O) == -4
+    assert pkg.attn_hadamard_quantize_e4m3(Q + 2, 4, 128, 1.0, O) == -6
+    assert pkg.attn_hadamard_quantize_e4m3(Q, 4, 128, 1.0, Q + 100) == -7

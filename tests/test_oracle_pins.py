@@ -293,3 +293,48 @@ def test_lse_merge_of_key_halves_is_causal_attention(oracle):
     ro, rl = oracle.attention(qb, kb, vb, oracle.BF16, tau, True, rows=np.arange(N, 2 * N))
     np.testing.assert_allclose(mo, ro, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(ml, rl, rtol=1e-12, atol=1e-12)
+
+
+# ---- Hadamard rotation (the step before FP8 quantization)
+def test_hadamard_matrix_small_orders_by_hand(oracle):
+    s = 1 / math.sqrt(2)
+    np.testing.assert_array_equal(oracle.hadamard_matrix(1), [[1.0]])
+    np.testing.assert_allclose(oracle.hadamard_matrix(2), [[s, s], [s, -s]], rtol=0, atol=1e-16)
+    h4 = 0.5 * np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]])
+    np.testing.assert_allclose(oracle.hadamard_matrix(4), h4, rtol=0, atol=1e-16)
+
+
+@pytest.mark.parametrize("n", [64, 128])
+def test_hadamard_matrix_orthogonal_symmetric_pm_entries(oracle, n):
+    h = oracle.hadamard_matrix(n)
+    np.testing.assert_allclose(h @ h.T, np.eye(n), rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(h, h.T)
+    np.testing.assert_allclose(np.abs(h), np.full((n, n), 1 / math.sqrt(n)), rtol=1e-15)
+    # Walsh functions: entry (i, j) has sign (-1)^popcount(i & j)
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    sign = np.vectorize(lambda a: -1.0 if bin(a).count("1") % 2 else 1.0)(i & j)
+    np.testing.assert_array_equal(np.sign(h), sign)
+
+
+@pytest.mark.parametrize("d", [128, 192])
+def test_hadamard_rows_are_isometric_and_self_inverse(oracle, d):
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((5, 3, d))
+    y = oracle.hadamard(x)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_allclose(oracle.hadamard(y), x, rtol=0, atol=1e-13)
+    # block structure: a unit vector in block b spreads only over block b
+    n = oracle.hadamard_block(d)
+    e = np.zeros(d)
+    e[d - 1] = 1.0
+    r = oracle.hadamard(e)
+    assert np.all(r[: d - n] == 0) and np.allclose(np.abs(r[d - n:]), 1 / math.sqrt(n))
+
+
+def test_hadamard_spreads_an_outlier_channel(oracle):
+    """The reason for the rotation: one dominant channel becomes d equal
+    entries, so the per-tensor FP8 scale no longer follows the outlier."""
+    x = np.zeros(128)
+    x[5] = 100.0
+    y = oracle.hadamard(x)
+    assert np.max(np.abs(y)) == pytest.approx(100.0 / math.sqrt(128), rel=1e-15)
