@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--hadamard", action="store_true",
                     help="also time the Hadamard rotation of Q, K, V (fp32) and of O (bf16) "
                          "at the workload's shape, the optional step before FP8 quantization")
+    ap.add_argument("--varlen", type=int, default=0,
+                    help="also time attn_fwd_varlen on the workload's tokens split into this "
+                         "many packed sequences of seeded random lengths")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one float32 elementwise copy of this many MiB before the "
                          "warmup (reads and writes exactly that many bytes): the reference "
@@ -154,6 +157,37 @@ def cpu_baseline(w, host, seconds, synth):
             "kind": "oracle", "full_run_estimate_s": round(spent * full_flops / flops, 1),
             "sample": "%d uniformly drawn query rows (chunks of at most S distinct rows) of head 0 (batch %d) of %s, causal, "
                       "fp64 oracle, %.1f s" % (nrows, w.B, w.name, spent)}
+
+
+def time_varlen(w, t, ds, pkg, torch, stream, nseq, reps):
+    """TFLOP/s of attn_fwd_varlen on the same tokens (batch 0's rows) cut into
+    `nseq` sequences with lognormal(0, 1) lengths (seeded) summing to S; the
+    causal FLOPs are sum_s L_s^2 (d_qk + d_v)."""
+    rng = np.random.default_rng(2024)
+    wts = np.exp(rng.standard_normal(nseq))
+    lens = np.maximum(1, np.floor(wts / wts.sum() * w.S)).astype(np.int64)
+    lens[-1] += w.S - lens.sum()
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(t[0].device)
+    pk = [x[0] for x in t]                       # [S, H, D] views of batch 0
+    o = torch.empty((w.S, w.H, w.d_v), dtype=torch.bfloat16, device=t[0].device)
+    lse = torch.empty((w.H, w.S), dtype=torch.float32, device=t[0].device)
+
+    def run():
+        pkg.flash_attn_varlen_func(*pk, cu, int(lens.max()), softmax_scale=w.softmax_scale,
+                                   causal=True, q_descale=ds[0], k_descale=ds[1],
+                                   v_descale=ds[2], out=o, lse=lse)
+    run()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        run()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    flops = float(np.sum(lens.astype(np.float64) ** 2)) * w.H * (w.d_qk + w.d_v)
+    return {"n_seqs": nseq, "min_len": int(lens.min()), "max_len": int(lens.max()),
+            "ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
 
 
 def time_hadamard(w, host, pkg, torch, stream, attn_ms, reps=10):
@@ -299,6 +333,8 @@ def main():
         "bitwise_identical_launches": identical,
         "inputs": input_stats(w, host),
     }
+    if args.varlen:
+        out["varlen"] = time_varlen(w, t, ds, pkg, torch, stream, args.varlen, args.steps)
     if args.hadamard:
         out["hadamard"] = time_hadamard(w, host, pkg, torch, stream, avg_kern)
     if not args.no_cpu:

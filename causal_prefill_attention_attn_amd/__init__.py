@@ -60,6 +60,9 @@ def load_library():
     lib.attn_fwd.restype = i32
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32,
                              f32, f32, f32, vp]
+    lib.attn_fwd_varlen.restype = i32
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32,
+                                    i32, i32, f32, f32, f32, vp]
     lib.attn_amax_f32.restype = i32
     lib.attn_amax_f32.argtypes = [vp, i64, vp, vp]
     lib.attn_quantize_e4m3.restype = i32
@@ -90,6 +93,14 @@ def attn_fwd(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale, causal, dtype,
     """Direct call of the C function on integer addresses; returns the status."""
     return int(load_library().attn_fwd(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale,
                                        causal, dtype, q_descale, k_descale, v_descale, stream))
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, n_seqs, total, max_seqlen, H, d_qk, d_v,
+                    softmax_scale, causal, dtype, q_descale=1.0, k_descale=1.0, v_descale=1.0,
+                    stream=None) -> int:
+    return int(load_library().attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, n_seqs, total,
+                                              max_seqlen, H, d_qk, d_v, softmax_scale, causal,
+                                              dtype, q_descale, k_descale, v_descale, stream))
 
 
 def attn_amax_f32(x, n, amax_out, stream=None) -> int:
@@ -176,6 +187,46 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_d
                   float(softmax_scale), int(bool(causal)), dt, float(q_descale),
                   float(k_descale), float(v_descale), _stream_handle(q.device))
     _check(st, "attn_fwd")
+    return out, lse
+
+
+def flash_attn_varlen_func(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=True,
+                           q_descale=1.0, k_descale=1.0, v_descale=1.0, out=None, lse=None,
+                           return_lse=True):
+    """Forward attention on packed sequences: q, k [total, H, d_qk], v
+    [total, H, d_v] (bfloat16, or FP8 e4m3 with per-tensor descales), with
+    sequence s in rows cu_seqlens[s] .. cu_seqlens[s+1]-1 (int32 CUDA tensor
+    of n_seqs + 1 prefix sums; max_seqlen the longest).  Returns ``(o, lse)``:
+    o bfloat16 [total, H, d_v], lse float32 [H, total] or None."""
+    torch = _torch()
+    dt = _element_dtype(q)
+    if _element_dtype(k) != dt or _element_dtype(v) != dt:
+        raise TypeError("q, k and v must share one element type")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 3 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous 3-D [total, H, D] CUDA tensor" % name)
+    if (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda
+            or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 CUDA tensor")
+    total, H, d_qk = q.shape
+    d_v = v.shape[2]
+    if tuple(k.shape) != (total, H, d_qk) or tuple(v.shape[:2]) != (total, H):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                             tuple(v.shape)))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_qk)
+    if out is None:
+        out = torch.empty((total, H, d_v), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    st = attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr() if lse is not None else None, cu_seqlens.data_ptr(),
+                         cu_seqlens.numel() - 1, total, int(max_seqlen), H, d_qk, d_v,
+                         float(softmax_scale), int(bool(causal)), dt, float(q_descale),
+                         float(k_descale), float(v_descale), _stream_handle(q.device))
+    _check(st, "attn_fwd_varlen")
     return out, lse
 
 

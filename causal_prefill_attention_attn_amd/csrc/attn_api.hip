@@ -41,13 +41,21 @@ const char* attn_status_string(int status) {
   }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-             int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale, int causal, int dtype,
-             float q_descale, float k_descale, float v_descale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launch of attn_fwd (cu null: B dense problems of S
+// rows, total = B*S) and attn_fwd_varlen (B packed sequences bounded by cu,
+// S the longest, total rows).
+int fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu,
+        int64_t total, int64_t B, int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale,
+        int causal, int dtype, float q_descale, float k_descale, float v_descale, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
-  if (B < 1 || S < 1 || H < 1) return ATTN_ERR_SHAPE;
-  // 32-bit indices inside the kernels: rows, heads, batch*head and the grid
-  if (S > INT32_MAX || H > INT32_MAX || B > INT32_MAX || B * H > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (B < 1 || S < 1 || H < 1 || total < 1) return ATTN_ERR_SHAPE;
+  // 32-bit indices inside the kernels: rows, heads, problem*head and the grid
+  if (S > INT32_MAX || H > INT32_MAX || B >= INT32_MAX || B * H > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (total > INT64_MAX / (H * 256)) return ATTN_ERR_SHAPE;
   const int64_t nqb = (S + 127) / 128;
   if (nqb * B * H > INT32_MAX) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8) return ATTN_ERR_DTYPE;
@@ -58,29 +66,52 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
       !(finite_positive(q_descale) && finite_positive(k_descale) && finite_positive(v_descale)))
     return ATTN_ERR_SCALE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      (lse && !aligned(lse, 4)))
+      (lse && !aligned(lse, 4)) || (cu && !aligned(cu, 4)))
     return ATTN_ERR_ALIGN;
   const int64_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 1;
-  // the kernels address one batch of q/k/v with 32-bit byte offsets (plus a
-  // tile of slack past the last row)
+  // the kernels address one problem of q/k/v with 32-bit byte offsets (plus
+  // a tile of slack past the last row)
   if ((S + 256) * H * d_qk * esz >= ((int64_t)1 << 32)) return ATTN_ERR_SHAPE;
-  const int64_t rows = B * S * H;
+  const int64_t rows = total * H;
   const int64_t nq = rows * d_qk * esz, nv = rows * d_v * esz, no = rows * d_v * 2;
-  const int64_t nl = B * H * S * 4;
+  const int64_t nl = total * H * 4;
   if (overlap(o, no, q, nq) || overlap(o, no, k, nq) || overlap(o, no, v, nv)) return ATTN_ERR_ALIAS;
   if (lse && (overlap(lse, nl, q, nq) || overlap(lse, nl, k, nq) || overlap(lse, nl, v, nv) ||
               overlap(lse, nl, o, no)))
+    return ATTN_ERR_ALIAS;
+  if (cu && (overlap(cu, (B + 1) * 4, o, no) || (lse && overlap(cu, (B + 1) * 4, lse, nl))))
     return ATTN_ERR_ALIAS;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int rc;
   if (dtype == ATTN_DTYPE_BF16)
-    rc = cpattn::launch_attn_bf16(q, k, v, o, lse, (int)B, (int)S, (int)H, d_qk, softmax_scale,
-                                  causal, st);
+    rc = cpattn::launch_attn_bf16(q, k, v, o, lse, cu, total, (int)B, (int)S, (int)H, d_qk,
+                                  softmax_scale, causal, st);
   else
-    rc = cpattn::launch_attn_fp8(q, k, v, o, lse, (int)B, (int)S, (int)H, d_qk, softmax_scale,
-                                 causal, q_descale, k_descale, v_descale, st);
+    rc = cpattn::launch_attn_fp8(q, k, v, o, lse, cu, total, (int)B, (int)S, (int)H, d_qk,
+                                 softmax_scale, causal, q_descale, k_descale, v_descale, st);
   return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+             int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale, int causal, int dtype,
+             float q_descale, float k_descale, float v_descale, void* stream) {
+  if (B >= 1 && S >= 1 && B > INT64_MAX / S) return ATTN_ERR_SHAPE;
+  return fwd(q, k, v, o, lse, nullptr, B >= 1 && S >= 1 ? B * S : 0, B, S, H, d_qk, d_v,
+             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, stream);
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int64_t n_seqs, int64_t total, int64_t max_seqlen,
+                    int64_t H, int d_qk, int d_v, float softmax_scale, int causal, int dtype,
+                    float q_descale, float k_descale, float v_descale, void* stream) {
+  if (!cu_seqlens) return ATTN_ERR_NULL;
+  return fwd(q, k, v, o, lse, cu_seqlens, total, n_seqs, max_seqlen, H, d_qk, d_v,
+             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, stream);
 }
 
 int attn_amax_f32(const float* x, int64_t n, float* amax_out, void* stream) {

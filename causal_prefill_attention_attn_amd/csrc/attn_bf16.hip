@@ -88,7 +88,8 @@ template <int DQK, int BN>
 __global__ void __launch_bounds__(kThreads, 1)
 attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
-                     float* __restrict__ lse, int S, int H, int BH, int nqb, float c_log2,
+                     float* __restrict__ lse, const int32_t* __restrict__ cu, int64_t total,
+                    int S_max, int H, int BH, int nqb, float c_log2,
                      int causal) {
   using LY = Layout<DQK, BN>;
   constexpr int kSteps = DQK / 16;                 // k-steps of the QK^T product
@@ -115,15 +116,19 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int bh = id % BH;
   const int b = bh / H;
   const int h = bh % H;
+  // rows of this problem (a batch entry or a packed sequence); S is its length
+  const SeqRows sr = seq_rows(cu, b, S_max, H, total);
+  const int S = sr.len;
   const int q0 = qb * kBM;
+  if (q0 >= S) return;  // past the end of a shorter sequence: nothing to do
   const int q0w = q0 + wave * 32;
   const uint32_t rsQK = (uint32_t)H * DQK * 2;  // bytes between rows
   const uint32_t rsV = (uint32_t)H * kVRow;
   const int64_t bstrQK = (int64_t)S * rsQK;
   const int64_t bstrV = (int64_t)S * rsV;
-  const uint8_t* qb8 = reinterpret_cast<const uint8_t*>(q) + b * bstrQK;
-  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(k) + b * bstrQK;
-  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(v) + b * bstrV;
+  const uint8_t* qb8 = reinterpret_cast<const uint8_t*>(q) + sr.row0 * rsQK;
+  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(k) + sr.row0 * rsQK;
+  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(v) + sr.row0 * rsV;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb8, (uint32_t)bstrQK);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb8, (uint32_t)bstrQK);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb8, (uint32_t)bstrV);
@@ -326,7 +331,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int qi = q0w + col;
   if (qi < S) {
     const float inv = 1.0f / l_tot;
-    __bf16* orow = o + ((int64_t)b * S * H + (int64_t)qi * H + h) * kDV;
+    __bf16* orow = o + ((sr.row0 + qi) * H + h) * kDV;
 #pragma unroll
     for (int d = 0; d < kDV / 32; ++d)
 #pragma unroll
@@ -337,26 +342,26 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         *reinterpret_cast<bf16x4*>(orow + d * 32 + g * 8 + half * 4) = w;
       }
     if (lse != nullptr && half == 0)
-      lse[(int64_t)bh * S + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      lse[sr.lse0 + h * sr.lse_hs + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
 }
 
 }  // namespace
 
-int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int S, int H, int d_qk, float softmax_scale, int causal,
-                     hipStream_t stream) {
+int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
+                     float softmax_scale, int causal, hipStream_t stream) {
   const int nqb = (S + kBM - 1) / kBM;
   const int BH = B * H;
   const dim3 grid((unsigned)nqb * (unsigned)BH);
   const float c_log2 = softmax_scale * 1.4426950408889634f;
   if (d_qk == 128)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 64>), grid, dim3(kThreads), 0, stream,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, S,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, cu, total, S,
                        H, BH, nqb, c_log2, causal);
   else
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<192, 32>), grid, dim3(kThreads), 0, stream,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, S,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, cu, total, S,
                        H, BH, nqb, c_log2, causal);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -28,6 +28,39 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Rows of one attention problem -- one batch entry of a dense [B,S,H,D]
+// tensor, or one sequence of a packed [total,H,D] tensor -- and where its LSE
+// goes (dense [B,H,S], packed [H,total]).
+struct SeqRows {
+  int64_t row0;    // first row of the problem in q/k/v/o
+  int len;         // its rows
+  int64_t lse0;    // LSE index of (head 0, row 0)
+  int64_t lse_hs;  // LSE stride between heads
+};
+// Problem b: dense when cu is null (S rows each), else packed with bounds
+// cu[b], cu[b+1] clamped to [0, total] and to S (the longest sequence), so
+// that any contents of cu give in-bounds accesses.
+__device__ __forceinline__ SeqRows seq_rows(const int32_t* cu, int b, int S, int H,
+                                            int64_t total) {
+  SeqRows r;
+  if (cu == nullptr) {
+    r.row0 = (int64_t)b * S;
+    r.len = S;
+    r.lse0 = (int64_t)b * H * S;
+    r.lse_hs = S;
+  } else {
+    int64_t a = cu[b], e = cu[b + 1];
+    a = a < 0 ? 0 : (a > total ? total : a);
+    e = e < a ? a : (e > total ? total : e);
+    if (e - a > S) e = a + S;
+    r.row0 = a;
+    r.len = (int)(e - a);
+    r.lse0 = a;
+    r.lse_hs = total;
+  }
+  return r;
+}
+
 // Buffer resource over `bytes` bytes from `base`: loads at byte offsets
 // >= bytes return zero (the hardware range check), which pads ragged tiles.
 // The whole offset goes in the VGPR operand so that it is range checked.

@@ -135,7 +135,8 @@ template <int DQK, int BN, bool kLean, int kOcc>
 __global__ void __launch_bounds__(256 * kOcc, 1)
 attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                     const uint8_t* __restrict__ v, __bf16* __restrict__ o,
-                    float* __restrict__ lse, int S, int H, int BH, int nqb, float c_log2,
+                    float* __restrict__ lse, const int32_t* __restrict__ cu, int64_t total,
+                    int S_max, int H, int BH, int nqb, float c_log2,
                     float v_descale, int causal, float lazy_log2) {
   using LY = Layout<DQK, BN>;
   constexpr int kWaves = 4 * kOcc;
@@ -160,16 +161,20 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int bh = id % BH;
   const int b = bh / H;
   const int h = bh % H;
+  // rows of this problem (a batch entry or a packed sequence); S is its length
+  const SeqRows sr = seq_rows(cu, b, S_max, H, total);
+  const int S = sr.len;
   const int q0 = qb * kBM;
+  if (q0 >= S) return;  // past the end of a shorter sequence: nothing to do
   const int q0w = q0 + wave * 32;
   const uint32_t rsQK = (uint32_t)H * DQK;  // bytes between consecutive rows
   const uint32_t rsV = (uint32_t)H * kDV;
   const int64_t bstrQK = (int64_t)S * rsQK;
   const int64_t bstrV = (int64_t)S * rsV;
   // one batch of q/k/v per buffer resource; rows >= S read as zero
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + b * bstrQK, (uint32_t)bstrQK);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + b * bstrQK, (uint32_t)bstrQK);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + b * bstrV, (uint32_t)bstrV);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + sr.row0 * rsQK, (uint32_t)bstrQK);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + sr.row0 * rsQK, (uint32_t)bstrQK);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + sr.row0 * rsV, (uint32_t)bstrV);
 
   // ---- Q^T operand: lane (query col, half) holds d = s*64 + half*32 .. +31
   i32x8 qreg[kSteps];
@@ -366,7 +371,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int qi = q0w + col;
   if (qi < S) {
     const float inv = v_descale / l_tot;
-    __bf16* orow = o + ((int64_t)b * S * H + (int64_t)qi * H + h) * kDV;
+    __bf16* orow = o + ((sr.row0 + qi) * H + h) * kDV;
 #pragma unroll
     for (int d = 0; d < kDV / 32; ++d)
 #pragma unroll
@@ -377,15 +382,16 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
         *reinterpret_cast<bf16x4*>(orow + d * 32 + g * 8 + half * 4) = w;
       }
     if (lse != nullptr && half == 0)
-      lse[(int64_t)bh * S + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      lse[sr.lse0 + h * sr.lse_hs + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
 }
 
 }  // namespace
 
-int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                    int S, int H, int d_qk, float softmax_scale, int causal, float q_descale,
-                    float k_descale, float v_descale, hipStream_t stream) {
+int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
+                    float softmax_scale, int causal, float q_descale, float k_descale,
+                    float v_descale, hipStream_t stream) {
   const int occ = 2;                      // waves per SIMD (register budget)
   const int bm = 128 * occ;               // query rows per workgroup
   const int nqb = (S + bm - 1) / bm;
@@ -405,8 +411,8 @@ int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float*
   }();
 #define CPATTN_LAUNCH_FP8(DQK, BN, LEAN, OCC)                                                     \
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, BN, LEAN, OCC>), grid, dim3(256 * OCC), 0, stream, \
-                     (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, S,   \
-                     H, BH, nqb, c_log2, v_descale, causal, lazy_log2)
+                     (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, cu, \
+                     total, S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2)
   if (d_qk == 128) {
     if (lean) CPATTN_LAUNCH_FP8(128, 64, true, 2);
     else CPATTN_LAUNCH_FP8(128, 64, false, 2);

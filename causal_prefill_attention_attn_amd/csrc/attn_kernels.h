@@ -6,15 +6,20 @@
 
 namespace cpattn {
 
-// BF16 q/k/v, d_qk in {128, 192}, d_v = 128.  Returns 0 or -1 (launch error).
-int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int S, int H, int d_qk, float softmax_scale, int causal,
-                     hipStream_t stream);
+// B problems of up to S rows each: dense [B,S,H,D] tensors when cu is null,
+// else B packed sequences of a [total,H,D] tensor bounded by cu[0..B]
+// (device), S being the longest.  Returns 0 or -1 (launch error).
+
+// BF16 q/k/v, d_qk in {128, 192}, d_v = 128.
+int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
+                     float softmax_scale, int causal, hipStream_t stream);
 
 // FP8 E4M3FN q/k/v with per-tensor descales, d_qk in {128, 192}, d_v = 128.
-int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                    int S, int H, int d_qk, float softmax_scale, int causal, float q_descale,
-                    float k_descale, float v_descale, hipStream_t stream);
+int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
+                    float softmax_scale, int causal, float q_descale, float k_descale,
+                    float v_descale, hipStream_t stream);
 
 int launch_amax_f32(const float* x, int64_t n, float* amax_out, hipStream_t stream);
 int launch_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out,

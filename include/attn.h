@@ -101,6 +101,34 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              float q_descale, float k_descale, float v_descale, void* stream);
 
 /*
+ * attn_fwd_varlen -- attn_fwd over a batch of sequences of different
+ * lengths packed along the token dimension, each attending only within
+ * itself (variable-length batches, which "Ce que couvrent les noyaux" on the
+ * ai-daily-news.org page lists among the kernels' future work).  Sequence s holds
+ * token rows cu_seqlens[s] .. cu_seqlens[s+1]-1 of every tensor.
+ *   q, k        device, [total, H, d_qk] contiguous; v [total, H, d_v]
+ *   o           device, [total, H, d_v] bf16 (written)
+ *   lse         device, [H, total] fp32 (written), or NULL
+ *   cu_seqlens  device, n_seqs + 1 int32 prefix sums: 0 = cu[0] <= cu[1] <=
+ *               ... <= cu[n_seqs] = total, each difference <= max_seqlen.
+ *               Read by the kernels, not validated on the host: other
+ *               contents are clamped to [0, total] and max_seqlen, which
+ *               keeps every access in bounds but gives unspecified results.
+ *               Empty sequences are allowed.
+ *   n_seqs      >= 1;  total >= 1;  max_seqlen >= 1 (the longest sequence)
+ *   the other arguments, alignment (cu_seqlens: 4 bytes), aliasing (o and lse
+ *   must not overlap q, k, v, cu_seqlens or each other), the per-sequence
+ *   4 GiB limit (with max_seqlen in place of S), determinism and the return
+ *   codes are those of attn_fwd.
+ * With n_seqs equal sequences of length L the results equal those of
+ * attn_fwd with B = n_seqs, S = L bit for bit (LSE in [H, total] order).
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int64_t n_seqs, int64_t total, int64_t max_seqlen,
+                    int64_t H, int d_qk, int d_v, float softmax_scale, int causal, int dtype,
+                    float q_descale, float k_descale, float v_descale, void* stream);
+
+/*
  * attn_amax_f32 -- largest magnitude of a float32 tensor, for choosing the
  * per-tensor FP8 descale (amax / 448).  The pages attribute most of the FP8
  * error to this quantization of Q, K and V ("Precisao, estabilidade e

@@ -32,7 +32,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == sorted(["attn_version", "attn_status_string", "attn_fwd", "attn_amax_f32",
+    assert names == sorted(["attn_version", "attn_status_string", "attn_fwd", "attn_fwd_varlen",
+                            "attn_amax_f32",
                             "attn_quantize_e4m3", "attn_hadamard_f32", "attn_hadamard_bf16",
                             "attn_hadamard_amax_f32", "attn_hadamard_quantize_e4m3"]), names
 
@@ -115,3 +116,26 @@ def test_hadamard_entry_points_reject(lib):
     assert pkg.attn_hadamard_quantize_e4m3(Q, 4, 100, 1.0, O) == -4
     assert pkg.attn_hadamard_quantize_e4m3(Q + 2, 4, 128, 1.0, O) == -6
     assert pkg.attn_hadamard_quantize_e4m3(Q, 4, 128, 1.0, Q + 100) == -7
+
+
+def test_varlen_entry_point_rejects(lib):
+    C = 0x60000000   # cu_seqlens
+
+    def call(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, cu_seqlens=C, n_seqs=3, total=1000, max_seqlen=500,
+                 H=4, d_qk=128, d_v=128, softmax_scale=0.1, causal=1, dtype=1, q_descale=1.0,
+                 k_descale=1.0, v_descale=1.0)
+        a.update(kw)
+        return pkg.attn_fwd_varlen(*a.values())
+    assert call(cu_seqlens=None) == -1
+    assert call(q=None) == -1
+    assert call(n_seqs=0) == -2
+    assert call(total=0) == -2
+    assert call(max_seqlen=0) == -2
+    assert call(max_seqlen=1 << 31) == -2
+    assert call(d_qk=64) == -4
+    assert call(dtype=5) == -3
+    assert call(softmax_scale=-1.0) == -5
+    assert call(cu_seqlens=C + 2) == -6
+    assert call(cu_seqlens=O + 16) == -7          # cu_seqlens inside o
+    assert call(lse=Q + 64) == -7
