@@ -4,7 +4,8 @@ One step = one attn_fwd call over the whole workload (every query block of
 every head), inputs resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload C4] [--gpus 1]
-                  [--cpu-seconds 12] [--no-cpu]
+                  [--cpu-seconds 12] [--no-cpu] [--varlen N] [--hadamard]
+                  [--energy SECONDS]
 
 Workloads (seeded synthetic inputs, recipes in causal_prefill_attention_attn_amd/synth.py):
   C4  (default) FP8 e4m3, B1 H32 S32768 d128, LLM-like activations
@@ -48,6 +49,9 @@ def parse():
     ap.add_argument("--varlen", type=int, default=0,
                     help="also time attn_fwd_varlen on the workload's tokens split into this "
                          "many packed sequences of seeded random lengths")
+    ap.add_argument("--energy", type=float, default=0.0,
+                    help="also run the kernel back to back for this many seconds and report "
+                         "joules from the GPU's energy accumulator, average watts and TFLOP/J")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one float32 elementwise copy of this many MiB before the "
                          "warmup (reads and writes exactly that many bytes): the reference "
@@ -188,6 +192,82 @@ def time_varlen(w, t, ds, pkg, torch, stream, nseq, reps):
     flops = float(np.sum(lens.astype(np.float64) ** 2)) * w.H * (w.d_qk + w.d_v)
     return {"n_seqs": nseq, "min_len": int(lens.min()), "max_len": int(lens.max()),
             "ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+
+
+def energy_run(step, flops, torch, seconds):
+    """Energy efficiency of the sustained kernel: launches back to back for
+    about `seconds`, bracketed by reads of the device's energy accumulator
+    (amdsmi, counter x resolution in microjoules) after a synchronize.  The
+    device is the one whose PCI bus matches torch's device 0.  The pages quote
+    TFLOP/J for their kernels on captured model layers (miraibroadcast page,
+    "ZYFA acelera atencao em ate 1,76x com menos erro"); here the workload is
+    the synthetic one being benchmarked."""
+    try:
+        import amdsmi
+    except Exception as e:  # pragma: no cover - depends on the image
+        return {"error": "amdsmi not importable: %s" % e}
+    try:
+        amdsmi.amdsmi_init()
+    except Exception as e:
+        return {"error": "amdsmi_init failed: %s" % e}
+    try:
+        bus = torch.cuda.get_device_properties(0).pci_bus_id
+        handles = amdsmi.amdsmi_get_processor_handles()
+        match = [h for h in handles
+                 if int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus]
+        if len(match) != 1:
+            return {"error": "no unique amdsmi device on PCI bus %#x (%d handles)"
+                    % (bus, len(handles))}
+        h = match[0]
+
+        def joules():
+            c = amdsmi.amdsmi_get_energy_count(h)
+            return c["energy_accumulator"] * c["counter_resolution"] * 1e-6
+
+        # time one launch to size the loop
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        per = max(time.perf_counter() - t0, 1e-4)
+        n = max(10, int(seconds / per))
+        watts, mhz = [], []
+
+        def sample():  # while launches are queued, so the GPU is busy
+            try:
+                p = amdsmi.amdsmi_get_power_info(h).get("current_socket_power")
+                if isinstance(p, (int, float)):
+                    watts.append(p)
+                c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
+                if isinstance(c, (int, float)):
+                    mhz.append(c)
+            except Exception:
+                pass
+
+        e0, t0 = joules(), time.perf_counter()
+        for i in range(n):
+            step()
+            if i % 64 == 31:
+                sample()
+            if i % 64 == 63:
+                torch.cuda.synchronize()  # keep the launch queue short
+        torch.cuda.synchronize()
+        e1, t1 = joules(), time.perf_counter()
+        j, sec = e1 - e0, t1 - t0
+        return {"launches": n, "seconds": round(sec, 3), "joules": round(j, 2),
+                "avg_watts": round(j / sec, 1) if sec > 0 else None,
+                "TFLOP/s": round(flops * n / sec / 1e12, 1),
+                "TFLOP/J": round(flops * n / j / 1e12, 3) if j > 0 else None,
+                "socket_watts_sampled_median": float(np.median(watts)) if watts else None,
+                "gfx_mhz_sampled_median": float(np.median(mhz)) if mhz else None,
+                "samples": len(watts)}
+    except Exception as e:
+        return {"error": "energy read failed: %s" % e}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def time_hadamard(w, host, pkg, torch, stream, attn_ms, reps=10):
@@ -335,6 +415,9 @@ def main():
     }
     if args.varlen:
         out["varlen"] = time_varlen(w, t, ds, pkg, torch, stream, args.varlen, args.steps)
+    if args.energy > 0:
+        log("bench: sustained run of %.0f s for energy" % args.energy)
+        out["energy"] = energy_run(step, flops, torch, args.energy)
     if args.hadamard:
         out["hadamard"] = time_hadamard(w, host, pkg, torch, stream, avg_kern)
     if not args.no_cpu:
