@@ -8,9 +8,11 @@ with it.
 The attention arithmetic lives in ``attn_oracle.c`` (plain C, binary64,
 OpenMP over query rows); this module builds that file with gcc and marshals
 numpy arrays through ctypes.  See the header of ``attn_oracle.c`` for the
-definition it computes and the passages of the pages it follows.  The one
-exception is the Hadamard rotation that may precede FP8 quantization
-(``hadamard``), a plain fp64 matrix product per block written here in numpy.
+definition it computes and the passages of the pages it follows.  Two
+functions are written here in numpy instead: the Hadamard rotation that may
+precede FP8 quantization (``hadamard``), a plain fp64 matrix product per
+block, and the decode step against a paged KV cache (``decode_paged``), a
+gather of the sequence's keys followed by the textbook softmax in fp64.
 """
 from __future__ import annotations
 
@@ -74,10 +76,17 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
+_bf16_table = None
+
+
 def decode_bf16(bits: np.ndarray) -> np.ndarray:
-    lib = _load()
-    flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
-    return np.array([lib.oracle_bf16_decode(int(b)) for b in flat], np.float64).reshape(np.shape(bits))
+    """bf16 bit patterns -> float64, through a table of all 65536 patterns
+    filled by the C decoder."""
+    global _bf16_table
+    if _bf16_table is None:
+        lib = _load()
+        _bf16_table = np.array([lib.oracle_bf16_decode(b) for b in range(65536)], np.float64)
+    return _bf16_table[np.asarray(bits, dtype=np.uint16)]
 
 
 def decode_e4m3(codes: np.ndarray) -> np.ndarray:
@@ -127,6 +136,53 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: int, tau: floa
                          _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_attn rejected its arguments")
+    return o, lse
+
+
+def decode_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                 block_table: np.ndarray, seq_lens: np.ndarray, dtype: int, tau: float,
+                 q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0):
+    """fp64 decode step against a paged KV cache: one new query token per
+    sequence attends to every cached key of its sequence.
+
+    Decode and paged KV caches are listed among the kernels' future work in
+    "Ce que couvrent les noyaux" on the ai-daily-news.org page; the step is
+    the last row of causal attention, so the definition is the textbook one,
+    o = softmax(tau * q.K^T) V and lse = log sum exp(tau * q.K^T), over the
+    sequence's keys 0 .. L-1 (the new token's own key and value are already
+    in the cache).  Readings: key j of sequence b sits in page
+    block_table[b, j // page_size], slot j % page_size; query head h reads
+    key/value head h // (H_q / H_kv); an empty sequence gives o = 0 and
+    lse = -inf.
+
+    q: [B, H_q, d_qk]; k_cache: [pages, page_size, H_kv, d_qk];
+    v_cache: [pages, page_size, H_kv, d_v]; raw encodings (uint16 bf16 bit
+    patterns for BF16, uint8 E4M3 codes for FP8) times their descales.
+    Returns (o [B, H_q, d_v], lse [B, H_q]) float64.
+    """
+    dec = decode_bf16 if dtype == BF16 else decode_e4m3
+    B, hq, dqk = q.shape
+    pages, ps, hkv, _ = k_cache.shape
+    dv = v_cache.shape[3]
+    assert hq % hkv == 0 and v_cache.shape[:3] == (pages, ps, hkv)
+    group = hq // hkv
+    qf = dec(q) * q_descale
+    o = np.zeros((B, hq, dv), np.float64)
+    lse = np.full((B, hq), -np.inf, np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        j = np.arange(n)
+        page = np.asarray(block_table[b], np.int64)[j // ps]
+        kb = dec(k_cache[page, j % ps]) * k_descale        # [n, H_kv, d_qk]
+        vb = dec(v_cache[page, j % ps]) * v_descale        # [n, H_kv, d_v]
+        for h in range(hq):
+            s = tau * (kb[:, h // group, :] @ qf[b, h])
+            m = s.max()
+            e = np.exp(s - m)
+            o[b, h] = (e @ vb[:, h // group, :]) / e.sum()
+            lse[b, h] = m + np.log(e.sum())
     return o, lse
 
 
