@@ -19,8 +19,11 @@ import os
 
 __all__ = [
     "ATTN_DTYPE_BF16", "ATTN_DTYPE_FP8", "AttnError", "lib_path", "load_library",
-    "attn_fwd", "attn_amax_f32", "attn_quantize_e4m3", "attn_status_string", "attn_version",
-    "flash_attn_func", "quantize_fp8",
+    "attn_fwd", "attn_fwd_varlen", "attn_amax_f32", "attn_quantize_e4m3", "attn_status_string",
+    "attn_version", "attn_hadamard_f32", "attn_hadamard_bf16", "attn_hadamard_amax_f32",
+    "attn_hadamard_quantize_e4m3", "attn_decode_paged", "attn_decode_workspace_bytes",
+    "flash_attn_func", "flash_attn_varlen_func", "flash_attn_decode_paged", "quantize_fp8",
+    "hadamard",
 ]
 
 ATTN_DTYPE_BF16 = 0
@@ -75,6 +78,11 @@ def load_library():
     lib.attn_hadamard_amax_f32.argtypes = [vp, i64, i32, vp, vp]
     lib.attn_hadamard_quantize_e4m3.restype = i32
     lib.attn_hadamard_quantize_e4m3.argtypes = [vp, i64, i32, f32, vp, vp]
+    lib.attn_decode_paged.restype = i32
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                      i32, i64, i64, i64, i64, f32, i32, f32, f32, f32, vp]
+    lib.attn_decode_workspace_bytes.restype = i64
+    lib.attn_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     _lib = lib
     return lib
 
@@ -128,6 +136,20 @@ def attn_hadamard_quantize_e4m3(x, rows, d, descale, out, stream=None) -> int:
 
 
 # ------------------------------------------------------------ torch helpers
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace,
+                      workspace_bytes, B, H_q, H_kv, d_qk, d_v, num_pages, page_size,
+                      max_pages_per_seq, max_seqlen, softmax_scale, dtype, q_descale=1.0,
+                      k_descale=1.0, v_descale=1.0, stream=None) -> int:
+    return int(load_library().attn_decode_paged(
+        q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace, workspace_bytes, B, H_q,
+        H_kv, d_qk, d_v, num_pages, page_size, max_pages_per_seq, max_seqlen, softmax_scale,
+        dtype, q_descale, k_descale, v_descale, stream))
+
+
+def attn_decode_workspace_bytes(B, H_q, H_kv, max_seqlen, d_v) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, H_q, H_kv, max_seqlen, d_v))
+
+
 def _torch():
     import torch
     return torch
@@ -227,6 +249,64 @@ def flash_attn_varlen_func(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, 
                          float(softmax_scale), int(bool(causal)), dt, float(q_descale),
                          float(k_descale), float(v_descale), _stream_handle(q.device))
     _check(st, "attn_fwd_varlen")
+    return out, lse
+
+
+def flash_attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seqlen,
+                            softmax_scale=None, q_descale=1.0, k_descale=1.0, v_descale=1.0,
+                            out=None, lse=None, workspace=None, return_lse=True):
+    """One decode step against a paged KV cache.
+
+    q [B, H_q, d_qk]; k_cache [pages, page_size, H_kv, d_qk]; v_cache
+    [pages, page_size, H_kv, d_v] (bfloat16, or FP8 e4m3 with per-tensor
+    descales); block_table [B, max_pages_per_seq] and seq_lens [B] int32 CUDA
+    tensors; max_seqlen bounds every seq_lens entry.  Query head h reads
+    key/value head h // (H_q // H_kv).  ``workspace``: a CUDA tensor of at
+    least attn_decode_workspace_bytes(...) bytes, allocated here when None.
+    Returns ``(o, lse)``: o bfloat16 [B, H_q, d_v], lse float32 [B, H_q] or
+    None."""
+    torch = _torch()
+    dt = _element_dtype(q)
+    if _element_dtype(k_cache) != dt or _element_dtype(v_cache) != dt:
+        raise TypeError("q and the caches must share one element type")
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B, H_q, d_qk] and the caches [pages, page_size, H_kv, d]")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seq_lens", seq_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous CUDA tensor" % name)
+    for name, t, nd in (("block_table", block_table, 2), ("seq_lens", seq_lens, 1)):
+        if t.dtype != torch.int32 or t.dim() != nd:
+            raise ValueError("%s must be a %d-D int32 tensor" % (name, nd))
+    B, H_q, d_qk = q.shape
+    pages, page_size, H_kv, _ = k_cache.shape
+    d_v = v_cache.shape[3]
+    if (tuple(k_cache.shape) != (pages, page_size, H_kv, d_qk)
+            or tuple(v_cache.shape[:3]) != (pages, page_size, H_kv)
+            or block_table.shape[0] != B or seq_lens.shape[0] != B):
+        raise ValueError("shape mismatch: q %s k_cache %s v_cache %s block_table %s seq_lens %s"
+                         % (tuple(q.shape), tuple(k_cache.shape), tuple(v_cache.shape),
+                            tuple(block_table.shape), tuple(seq_lens.shape)))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_qk)
+    need = attn_decode_workspace_bytes(B, H_q, H_kv, int(max_seqlen), d_v)
+    _check(need if need < 0 else 0, "attn_decode_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, H_q, d_v), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    st = attn_decode_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                           lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), B, H_q, H_kv, d_qk,
+                           d_v, pages, page_size, block_table.shape[1], int(max_seqlen),
+                           float(softmax_scale), dt, float(q_descale), float(k_descale),
+                           float(v_descale), _stream_handle(q.device))
+    _check(st, "attn_decode_paged")
     return out, lse
 
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcpattn.so")
-SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_fp8.hip", "quant.hip", "hadamard.hip"]
+SOURCES = ["attn_api.hip", "attn_bf16.hip", "attn_fp8.hip", "quant.hip", "hadamard.hip", "decode.hip"]
 HEADERS = ["attn_device.h", "attn_kernels.h"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

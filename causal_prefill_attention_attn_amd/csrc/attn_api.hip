@@ -24,7 +24,7 @@ bool overlap(const void* p, int64_t np, const void* q, int64_t nq) {
 
 extern "C" {
 
-int attn_version(void) { return 100; }
+int attn_version(void) { return 200; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -37,6 +37,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_ALIAS: return "o or lse overlaps an input or the other output";
     case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes";
     default: return "unknown status";
   }
 }
@@ -190,6 +191,106 @@ int attn_hadamard_quantize_e4m3(const float* x, int64_t rows, int d, float desca
                                           reinterpret_cast<hipStream_t>(stream)) == 0
              ? ATTN_OK
              : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Sizes of attn_decode_paged that do not involve buffers.
+int decode_sizes(int64_t B, int64_t H_q, int64_t H_kv, int64_t max_seqlen, int d_v) {
+  if (B < 1 || B > 65535 || H_kv < 1 || H_kv > 65535 || H_q < 1 || max_seqlen < 1 ||
+      max_seqlen >= ((int64_t)1 << 30))
+    return ATTN_ERR_SHAPE;
+  if (H_q % H_kv != 0 || B * H_q > INT32_MAX) return ATTN_ERR_SHAPE;
+  const int64_t g = H_q / H_kv;
+  if (!(g == 1 || g == 2 || g == 4 || g == 8) || d_v != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t attn_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t max_seqlen,
+                                    int d_v) {
+  const int rc = decode_sizes(B, H_q, H_kv, max_seqlen, d_v);
+  if (rc != ATTN_OK) return rc;
+  return cpattn::decode_workspace_bytes(B, H_q, H_kv, max_seqlen);
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                      void* workspace, int64_t workspace_bytes, int64_t B, int64_t H_q,
+                      int64_t H_kv, int d_qk, int d_v, int64_t num_pages, int64_t page_size,
+                      int64_t max_pages_per_seq, int64_t max_seqlen, float softmax_scale,
+                      int dtype, float q_descale, float k_descale, float v_descale,
+                      void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !workspace)
+    return ATTN_ERR_NULL;
+  int rc = decode_sizes(B, H_q, H_kv, max_seqlen, d_v);
+  if (rc != ATTN_OK) return rc;
+  if (page_size < 16 || page_size > ((int64_t)1 << 20) || (page_size & (page_size - 1)) != 0 ||
+      num_pages < 1 || num_pages > INT32_MAX || max_pages_per_seq < 1 ||
+      max_pages_per_seq > INT32_MAX || max_seqlen > max_pages_per_seq * page_size ||
+      B * max_pages_per_seq > ((int64_t)1 << 40))
+    return ATTN_ERR_SHAPE;
+  if (num_pages > INT64_MAX / (page_size * H_kv * 192 * 2)) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8) return ATTN_ERR_DTYPE;
+  if (d_qk != 128 && d_qk != 192) return ATTN_ERR_UNSUPPORTED;
+  if (!finite_positive(softmax_scale)) return ATTN_ERR_SCALE;
+  if (dtype == ATTN_DTYPE_FP8 &&
+      !(finite_positive(q_descale) && finite_positive(k_descale) && finite_positive(v_descale)))
+    return ATTN_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)) ||
+      !aligned(workspace, 16))
+    return ATTN_ERR_ALIGN;
+  const int64_t need = cpattn::decode_workspace_bytes(B, H_q, H_kv, max_seqlen);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  const int64_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 1;
+  const int64_t nq = B * H_q * d_qk * esz;
+  const int64_t nk = num_pages * page_size * H_kv * d_qk * esz;
+  const int64_t nv = num_pages * page_size * H_kv * d_v * esz;
+  const int64_t nt = B * max_pages_per_seq * 4, nl = B * 4;
+  const int64_t no = B * H_q * d_v * 2, nlse = B * H_q * 4;
+  struct Buf { const void* p; int64_t n; };
+  const Buf inputs[] = {{q, nq}, {k_cache, nk}, {v_cache, nv}, {block_table, nt}, {seq_lens, nl}};
+  const Buf outputs[] = {{o, no}, {lse, nlse}, {workspace, need}};
+  for (const Buf& out : outputs) {
+    if (!out.p) continue;
+    for (const Buf& in : inputs)
+      if (overlap(out.p, out.n, in.p, in.n)) return ATTN_ERR_ALIAS;
+  }
+  if ((lse && overlap(o, no, lse, nlse)) || overlap(o, no, workspace, need) ||
+      (lse && overlap(lse, nlse, workspace, need)))
+    return ATTN_ERR_ALIAS;
+
+  cpattn::DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.B = B;
+  a.Hq = H_q;
+  a.Hkv = H_kv;
+  a.d_qk = d_qk;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.max_pages_per_seq = max_pages_per_seq;
+  a.max_seqlen = max_seqlen;
+  a.softmax_scale = softmax_scale;
+  a.dtype_fp8 = dtype == ATTN_DTYPE_FP8;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  cpattn::decode_split_policy(B, H_kv, max_seqlen, &a.split, &a.nsplit);
+  rc = cpattn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+  return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -34,4 +34,28 @@ int launch_hadamard_amax(const float* x, int64_t rows, int d, float* amax_out,
 int launch_hadamard_quantize(const float* x, int64_t rows, int d, float descale, uint8_t* out,
                              hipStream_t stream);
 
+// Decode step against a paged KV cache (decode.hip).  split/nsplit come from
+// decode_split_policy; the workspace holds B*Hq*nsplit partial outputs of 128
+// floats followed by B*Hq*nsplit partial log-sum-exps.
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  void* workspace;
+  int64_t B, Hq, Hkv;
+  int d_qk;
+  int64_t num_pages, page_size, max_pages_per_seq, max_seqlen;
+  float softmax_scale;
+  bool dtype_fp8;
+  float q_descale, k_descale, v_descale;
+  int split, nsplit;
+};
+void decode_split_policy(int64_t B, int64_t Hkv, int64_t max_seqlen, int* split, int* nsplit);
+int64_t decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seqlen);
+int launch_decode(const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace cpattn

@@ -1,0 +1,425 @@
+// Decode step against a paged KV cache (gfx950): one new query token per
+// sequence attends to every cached key of its sequence.  Decode and paged KV
+// caches are the kernels' stated future work ("Ce que couvrent les noyaux",
+// ai-daily-news.org page); the step is the last row of causal attention,
+// o = softmax(tau q.K^T) V over keys 0 .. L-1.
+//
+// Paged cache: K [pages, page_size, H_kv, d_qk], V [pages, page_size, H_kv,
+// 128]; key j of sequence b is slot j % page_size of page
+// table[b][j / page_size].  Query head h reads key/value head h / G,
+// G = H_q / H_kv.
+//
+// One query row per head makes this a matrix-vector product: 2 FLOPs per
+// cached element (G per element with grouped heads), far below the matrix
+// cores' ridge, so the kernel is bound by HBM and runs on the vector ALU in
+// fp32.  What matters is streaming the cache with wide, coalesced loads and
+// enough workgroups in flight.
+//
+// Split over keys.  Workgroup (split s, key/value head hk, sequence b) takes
+// keys [s*split, min((s+1)*split, L)) for the G query heads of hk, and leaves
+// per head a partial output normalised by its own sum plus the partial's
+// log-sum-exp.  decode_merge_kernel combines the partials of each head in
+// split order, so results do not depend on timing.
+//
+// Inside a workgroup: 4 waves; a wave takes tiles of 16 consecutive keys
+// (tiles w, w+4, ...), which lie in one page since pages hold a multiple of
+// 16 keys and splits start at multiples of 64.  Lane group g (16 lanes) holds
+// key g of each 4-key step; its 16 lanes share the key's row, so a score is a
+// 16-lane sum (four DPP adds) and each lane keeps 8 of the 128 output values.
+// Each lane group runs its own online softmax; the 16 streams of a workgroup
+// are merged at the end.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace cpattn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kDV = 128;
+constexpr int kTile = 16;  // keys per wave tile: 4 lane groups x 4 steps
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNoKeys = -1e30f;  // running max of a stream that has seen no key
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Sum over the 16 lanes of a row: xor 1 and xor 2 (quad permutes), then the
+// half-row and row mirrors.  Every lane ends with the same value.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+  return x;
+}
+
+// One lane's share of a row of `d` elements: elements 8*sub .. 8*sub+7 of the
+// first 128, and for d = 192 elements 128 + 4*sub .. +3 as well, as raw words
+// (bf16 pairs, or four e4m3 codes).
+template <int DQK, bool kFP8>
+struct RowPart {
+  static constexpr int kA = kFP8 ? 2 : 4;              // words of the first 128 elements
+  static constexpr int kB = DQK == 192 ? kA / 2 : 0;   // words of the last 64
+  uint32_t a[kA];
+  uint32_t b[kB > 0 ? kB : 1];
+};
+
+template <int DQK, bool kFP8>
+__device__ __forceinline__ RowPart<DQK, kFP8> load_row(const uint8_t* row, int sub) {
+  constexpr int esz = kFP8 ? 1 : 2;
+  RowPart<DQK, kFP8> r;
+  if constexpr (kFP8) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(row + sub * 8);
+    r.a[0] = x[0];
+    r.a[1] = x[1];
+    if constexpr (DQK == 192) r.b[0] = *reinterpret_cast<const uint32_t*>(row + 128 + sub * 4);
+  } else {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(row + sub * 16);
+    r.a[0] = x[0];
+    r.a[1] = x[1];
+    r.a[2] = x[2];
+    r.a[3] = x[3];
+    if constexpr (DQK == 192) {
+      const u32x2 y = *reinterpret_cast<const u32x2*>(row + 128 * esz + sub * 8);
+      r.b[0] = y[0];
+      r.b[1] = y[1];
+    }
+  }
+  return r;
+}
+
+// Words -> fp32 values, in element order.
+__device__ __forceinline__ void bf16_words(const uint32_t* w, int n, float* out) {
+  for (int i = 0; i < n; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void e4m3_words(const uint32_t* w, int n, float* out) {
+  for (int i = 0; i < n; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    out[4 * i] = lo[0];
+    out[4 * i + 1] = lo[1];
+    out[4 * i + 2] = hi[0];
+    out[4 * i + 3] = hi[1];
+  }
+}
+
+// e4m3 words -> bf16 pairs (every e4m3 value is exact in bf16), element order.
+__device__ __forceinline__ void e4m3_to_bf16_words(const uint32_t* w, int n, uint32_t* out) {
+  for (int i = 0; i < n; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    const bf16x2 a = {(__bf16)lo[0], (__bf16)lo[1]};
+    const bf16x2 b = {(__bf16)hi[0], (__bf16)hi[1]};
+    out[2 * i] = __builtin_bit_cast(uint32_t, a);
+    out[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
+  }
+}
+
+// A lane's share of a query or key row as bf16 pairs: the raw words for
+// bf16, the converted codes for e4m3.
+template <int DQK, bool kFP8>
+struct Pairs {
+  static constexpr int kN = DQK / 32;  // bf16 pairs per lane
+  uint32_t w[kN];
+};
+template <int DQK, bool kFP8>
+__device__ __forceinline__ Pairs<DQK, kFP8> row_pairs(const RowPart<DQK, kFP8>& r) {
+  using R = RowPart<DQK, kFP8>;
+  Pairs<DQK, kFP8> p;
+  if constexpr (kFP8) {
+    e4m3_to_bf16_words(r.a, R::kA, p.w);
+    if constexpr (R::kB > 0) e4m3_to_bf16_words(r.b, R::kB, p.w + 2 * R::kA);
+  } else {
+#pragma unroll
+    for (int i = 0; i < R::kA; ++i) p.w[i] = r.a[i];
+#pragma unroll
+    for (int i = 0; i < R::kB; ++i) p.w[R::kA + i] = r.b[i];
+  }
+  return p;
+}
+
+template <int DQK, bool kFP8>
+__device__ __forceinline__ void row_values(const RowPart<DQK, kFP8>& r, float* out) {
+  using R = RowPart<DQK, kFP8>;
+  if constexpr (kFP8) {
+    e4m3_words(r.a, R::kA, out);
+    if constexpr (R::kB > 0) e4m3_words(r.b, R::kB, out + 4 * R::kA);
+  } else {
+    bf16_words(r.a, R::kA, out);
+    if constexpr (R::kB > 0) bf16_words(r.b, R::kB, out + 2 * R::kA);
+  }
+}
+
+template <int DQK, int G, bool kFP8>
+__global__ void __launch_bounds__(64 * kWaves)
+decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
+                    const uint8_t* __restrict__ vc, const int32_t* __restrict__ table,
+                    const int32_t* __restrict__ lens, float* __restrict__ opart,
+                    float* __restrict__ lpart, int Hkv, int maxp, int npages, int ps_log2,
+                    int lcap, int split, int nsplit, float c_log2, float v_descale) {
+  constexpr int esz = kFP8 ? 1 : 2;
+  const int sp = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  int L = lens[b];
+  L = L < 0 ? 0 : (L > lcap ? lcap : L);
+  const int k0 = sp * split;
+  if (k0 >= L) return;  // whole workgroup: this split is past the sequence's end
+  const int k1 = min(L, k0 + split);
+  const int ntile = (k1 - k0 + kTile - 1) / kTile;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 4, sub = lane & 15;
+  const int Hq = Hkv * G;
+  const int ps = 1 << ps_log2;
+
+  // the G query rows as bf16 pairs: scores are dot2 sums of pairs in fp32
+  using QP = Pairs<DQK, kFP8>;
+  QP qp[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint8_t* qrow = q + ((int64_t)b * Hq + hk * G + g) * DQK * esz;
+    qp[g] = row_pairs<DQK, kFP8>(load_row<DQK, kFP8>(qrow, sub));
+  }
+
+  const int64_t rsK = (int64_t)Hkv * DQK * esz;  // bytes between slots
+  const int64_t rsV = (int64_t)Hkv * kDV * esz;
+  const uint8_t* kbase = kc + (int64_t)hk * DQK * esz;
+  const uint8_t* vbase = vc + (int64_t)hk * kDV * esz;
+  const int32_t* trow = table + (int64_t)b * maxp;
+
+  struct Tile {
+    RowPart<DQK, kFP8> k[4];
+    RowPart<128, kFP8> v[4];
+  };
+  // rows of tile t: keys key0 + 4r + grp; keys at or past k1 read the tile's
+  // first row (a valid key) and are masked below
+  auto load_tile = [&](int t) {
+    Tile x;
+    const int key0 = k0 + t * kTile;
+    int page = trow[key0 >> ps_log2];
+    page = page < 0 ? 0 : (page >= npages ? npages - 1 : page);
+    const int64_t slot0 = (int64_t)page * ps + (key0 & (ps - 1));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int dk = 4 * r + grp;
+      const int64_t slot = slot0 + (key0 + dk < k1 ? dk : 0);
+      x.k[r] = load_row<DQK, kFP8>(kbase + slot * rsK, sub);
+      x.v[r] = load_row<128, kFP8>(vbase + slot * rsV, sub);
+    }
+    return x;
+  };
+
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNoKeys;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[g][e] = 0.0f;
+  }
+
+  int t = wave;
+  Tile cur;
+  if (t < ntile) cur = load_tile(t);
+  for (; t < ntile; t += kWaves) {
+    Tile nxt = cur;
+    if (t + kWaves < ntile) nxt = load_tile(t + kWaves);
+    const int key0 = k0 + t * kTile;
+    float sc[4][G];  // logits in log2 units, then probabilities
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool valid = key0 + 4 * r + grp < k1;
+      const QP kp = row_pairs<DQK, kFP8>(cur.k[r]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < QP::kN; ++i)
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qp[g].w[i]),
+                                                __builtin_bit_cast(bf16x2, kp.w[i]), acc, false);
+        acc = row16_sum(acc) * c_log2;
+        sc[r][g] = valid ? acc : -INFINITY;
+      }
+    }
+    float alpha[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mx = fmaxf(fmaxf(sc[0][g], sc[1][g]), fmaxf(sc[2][g], sc[3][g]));
+      const float mn = fmaxf(m[g], mx);
+      alpha[g] = __builtin_amdgcn_exp2f(m[g] - mn);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r][g] = __builtin_amdgcn_exp2f(sc[r][g] - mn);
+      l[g] = fmaf(l[g], alpha[g], (sc[0][g] + sc[1][g]) + (sc[2][g] + sc[3][g]));
+      m[g] = mn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[g][e] *= alpha[g];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float vv[8];
+      row_values<128, kFP8>(cur.v[r], vv);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] = fmaf(sc[r][g], vv[e], o[g][e]);
+    }
+    cur = nxt;
+  }
+
+  // merge the four lane groups of the wave (lanes sub, sub+16, sub+32, sub+48
+  // hold the same output columns)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float M = fmaxf(m[g], __shfl_xor(m[g], 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float w = __builtin_amdgcn_exp2f(m[g] - M);
+    float lw = l[g] * w;
+    lw += __shfl_xor(lw, 16);
+    lw += __shfl_xor(lw, 32);
+    l[g] = lw;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = o[g][e] * w;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      o[g][e] = x;
+    }
+    m[g] = M;
+  }
+
+  // merge the waves through LDS, in wave order
+  __shared__ float sO[kWaves][G][kDV];
+  __shared__ float sM[kWaves][G], sL[kWaves][G];
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sO[wave][g][sub * 8 + e] = o[g][e];
+      if (sub == 0) {
+        sM[wave][g] = m[g];
+        sL[wave][g] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * kDV; i += 64 * kWaves) {
+    const int g = i / kDV, d = i % kDV;
+    float M = sM[0][g];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sM[w][g]);
+    float lt = 0.0f, ot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(sM[w][g] - M);
+      lt = fmaf(sL[w][g], f, lt);
+      ot = fmaf(sO[w][g][d], f, ot);
+    }
+    // key k0 is valid, so lt > 0
+    const int64_t ph = ((int64_t)b * Hq + hk * G + g) * nsplit + sp;
+    opart[ph * kDV + d] = ot / lt * v_descale;
+    if (d == 0) lpart[ph] = (M + __builtin_amdgcn_logf(lt)) / kLog2e;
+  }
+}
+
+// o[b, h] = sum_s e^{lse_s} o_s / sum_s e^{lse_s} over the splits that hold
+// keys of sequence b, in split order; lse = log sum_s e^{lse_s}.  An empty
+// sequence gives o = 0 and lse = -inf.
+__global__ void __launch_bounds__(kDV)
+decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ lpart,
+                    const int32_t* __restrict__ lens, __bf16* __restrict__ o,
+                    float* __restrict__ lse, int Hq, int lcap, int split, int nsplit) {
+  const int bh = blockIdx.x;
+  const int b = bh / Hq;
+  const int d = threadIdx.x;
+  int L = lens[b];
+  L = L < 0 ? 0 : (L > lcap ? lcap : L);
+  const int ns = (L + split - 1) / split;
+  const float* lp = lpart + (int64_t)bh * nsplit;
+  const float* op = opart + (int64_t)bh * nsplit * kDV;
+  if (ns == 0) {
+    o[(int64_t)bh * kDV + d] = (__bf16)0.0f;
+    if (lse != nullptr && d == 0) lse[bh] = -INFINITY;
+    return;
+  }
+  float M = lp[0];
+  for (int s = 1; s < ns; ++s) M = fmaxf(M, lp[s]);
+  float wsum = 0.0f, acc = 0.0f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = expf(lp[s] - M);
+    wsum += w;
+    acc = fmaf(w, op[(int64_t)s * kDV + d], acc);
+  }
+  o[(int64_t)bh * kDV + d] = (__bf16)(acc / wsum);
+  if (lse != nullptr && d == 0) lse[bh] = M + logf(wsum);
+}
+
+template <int DQK, int G, bool kFP8>
+void launch_split(const DecodeArgs& a, float* opart, float* lpart, float c_log2,
+                  hipStream_t stream) {
+  int ps_log2 = 0;
+  while ((int64_t(1) << ps_log2) < a.page_size) ++ps_log2;
+  hipLaunchKernelGGL((decode_split_kernel<DQK, G, kFP8>),
+                     dim3(a.nsplit, (unsigned)a.Hkv, (unsigned)a.B), dim3(64 * kWaves), 0, stream,
+                     (const uint8_t*)a.q, (const uint8_t*)a.k_cache, (const uint8_t*)a.v_cache,
+                     a.block_table, a.seq_lens, opart, lpart, (int)a.Hkv,
+                     (int)a.max_pages_per_seq, (int)a.num_pages, ps_log2, (int)a.max_seqlen,
+                     a.split, a.nsplit, c_log2, a.dtype_fp8 ? a.v_descale : 1.0f);
+}
+
+template <int DQK, bool kFP8>
+void launch_split_g(const DecodeArgs& a, int G, float* opart, float* lpart, float c_log2,
+                    hipStream_t stream) {
+  switch (G) {
+    case 1: launch_split<DQK, 1, kFP8>(a, opart, lpart, c_log2, stream); break;
+    case 2: launch_split<DQK, 2, kFP8>(a, opart, lpart, c_log2, stream); break;
+    case 4: launch_split<DQK, 4, kFP8>(a, opart, lpart, c_log2, stream); break;
+    default: launch_split<DQK, 8, kFP8>(a, opart, lpart, c_log2, stream); break;
+  }
+}
+
+}  // namespace
+
+void decode_split_policy(int64_t B, int64_t Hkv, int64_t max_seqlen, int* split, int* nsplit) {
+  // about 2048 workgroups (8 per CU) when the sequences are long enough;
+  // splits of at least 256 keys, a multiple of 64
+  const int64_t per = B * Hkv;
+  const int64_t want = (2048 + per - 1) / per;
+  int64_t sp = (max_seqlen + want - 1) / want;
+  sp = (sp + 63) / 64 * 64;
+  if (sp < 256) sp = 256;
+  *split = (int)sp;
+  *nsplit = (int)((max_seqlen + sp - 1) / sp);
+}
+
+int64_t decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seqlen) {
+  int split, nsplit;
+  decode_split_policy(B, Hkv, max_seqlen, &split, &nsplit);
+  return B * Hq * nsplit * (kDV + 1) * 4;
+}
+
+int launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  float* opart = reinterpret_cast<float*>(a.workspace);
+  float* lpart = opart + a.B * a.Hq * a.nsplit * kDV;
+  const float c_log2 = a.softmax_scale * kLog2e * (a.dtype_fp8 ? a.q_descale * a.k_descale : 1.0f);
+  const int G = (int)(a.Hq / a.Hkv);
+  if (a.dtype_fp8) {
+    if (a.d_qk == 128) launch_split_g<128, true>(a, G, opart, lpart, c_log2, stream);
+    else launch_split_g<192, true>(a, G, opart, lpart, c_log2, stream);
+  } else {
+    if (a.d_qk == 128) launch_split_g<128, false>(a, G, opart, lpart, c_log2, stream);
+    else launch_split_g<192, false>(a, G, opart, lpart, c_log2, stream);
+  }
+  if (hipGetLastError() != hipSuccess) return -1;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(kDV), 0, stream,
+                     opart, lpart, a.seq_lens, (__bf16*)a.o, a.lse, (int)a.Hq,
+                     (int)a.max_seqlen, a.split, a.nsplit);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace cpattn

@@ -47,6 +47,7 @@ extern "C" {
 #define ATTN_ERR_ALIGN (-6)       /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
 #define ATTN_ERR_ALIAS (-7)       /* an output buffer overlaps an input or the other output */
 #define ATTN_ERR_LAUNCH (-8)      /* the HIP runtime rejected the kernel launch */
+#define ATTN_ERR_WORKSPACE (-9)   /* workspace smaller than attn_decode_workspace_bytes */
 
 /* element types of q, k, v */
 #define ATTN_DTYPE_BF16 0 /* bfloat16 */
@@ -192,6 +193,61 @@ int attn_hadamard_bf16(const void* x, int64_t rows, int d, void* y, void* stream
 int attn_hadamard_amax_f32(const float* x, int64_t rows, int d, float* amax_out, void* stream);
 int attn_hadamard_quantize_e4m3(const float* x, int64_t rows, int d, float descale, uint8_t* out,
                                 void* stream);
+
+/*
+ * attn_decode_paged -- one decode step against a paged KV cache: the new
+ * query token of each sequence attends to every cached key of its sequence,
+ *
+ *   o[b,h] = softmax(tau * q[b,h] . K_b^T) V_b,   lse[b,h] = log sum_j exp(...)
+ *
+ * over keys j = 0 .. L_b - 1 (the new token's own key and value already
+ * written to the cache).  Decode and paged KV caches are listed among the
+ * kernels' future work ("Ce que couvrent les noyaux" on the
+ * ai-daily-news.org page); this is the last row of causal attention.
+ *   q            device, [B, H_q, d_qk] contiguous (bf16, or e4m3 codes)
+ *   k_cache      device, [num_pages, page_size, H_kv, d_qk]
+ *   v_cache      device, [num_pages, page_size, H_kv, d_v]
+ *   block_table  device, [B, max_pages_per_seq] int32: key j of sequence b is
+ *                slot j % page_size of page block_table[b, j / page_size]
+ *   seq_lens     device, [B] int32, 0 <= L_b <= max_seqlen
+ *   o            device, [B, H_q, d_v] bf16 (written)
+ *   lse          device, [B, H_q] fp32 (written), or NULL
+ *   workspace    device, at least attn_decode_workspace_bytes(B, H_q, H_kv,
+ *                max_seqlen, d_v) bytes, 16-byte aligned; scratch for the
+ *                partial results of the key splits, overwritten
+ *   B            1 .. 65535;  H_kv 1 .. 65535;  H_q = G * H_kv, G in {1,2,4,8}
+ *                (query head h reads key/value head h / G); B * H_q < 2^31
+ *   d_qk, d_v    (128, 128) or (192, 128)
+ *   page_size    a power of two, 16 .. 2^20;  num_pages >= 1
+ *   max_pages_per_seq >= 1;  max_seqlen 1 .. max_pages_per_seq * page_size
+ *                and < 2^30 (the longest sequence; sizes the key splits)
+ *   softmax_scale, dtype, q/k/v_descale as in attn_fwd.
+ * block_table and seq_lens are read by the kernels, not on the host: page
+ * numbers are clamped to [0, num_pages) and lengths to [0, max_seqlen], which
+ * keeps every access in bounds but gives unspecified results for other
+ * contents.  Slots past the end of a sequence are never read.  An empty
+ * sequence gives o = 0 and lse = -inf.  Alignment: q, k_cache, v_cache, o
+ * 16 bytes, block_table, seq_lens, lse 4 bytes.  o, lse and workspace must not
+ * overlap an input or each other.  Arithmetic is fp32 (scores as sums of
+ * bf16 products, which holds e4m3 values exactly); the keys are split into
+ * ranges whose partial results merge in a fixed order, so repeated calls
+ * give bitwise identical results.
+ */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                      void* workspace, int64_t workspace_bytes, int64_t B, int64_t H_q,
+                      int64_t H_kv, int d_qk, int d_v, int64_t num_pages, int64_t page_size,
+                      int64_t max_pages_per_seq, int64_t max_seqlen, float softmax_scale,
+                      int dtype, float q_descale, float k_descale, float v_descale,
+                      void* stream);
+
+/*
+ * attn_decode_workspace_bytes -- workspace attn_decode_paged needs for these
+ * sizes (it depends on them only, not on the cache contents), or a negative
+ * status code when they are out of range (see attn_decode_paged).
+ */
+int64_t attn_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t max_seqlen,
+                                    int d_v);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     assert names == sorted(["attn_version", "attn_status_string", "attn_fwd", "attn_fwd_varlen",
                             "attn_amax_f32",
                             "attn_quantize_e4m3", "attn_hadamard_f32", "attn_hadamard_bf16",
-                            "attn_hadamard_amax_f32", "attn_hadamard_quantize_e4m3"]), names
+                            "attn_hadamard_amax_f32", "attn_hadamard_quantize_e4m3",
+                            "attn_decode_paged", "attn_decode_workspace_bytes"]), names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -45,8 +46,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert pkg.attn_version() >= 100
-    for code in range(0, -9, -1):
+    assert pkg.attn_version() >= 200
+    for code in range(0, -10, -1):
         s = pkg.attn_status_string(code)
         assert s and s != "unknown status"
     assert pkg.attn_status_string(-100) == "unknown status"
@@ -139,3 +140,52 @@ def test_varlen_entry_point_rejects(lib):
     assert call(cu_seqlens=C + 2) == -6
     assert call(cu_seqlens=O + 16) == -7          # cu_seqlens inside o
     assert call(lse=Q + 64) == -7
+
+
+def test_decode_workspace_bytes(lib):
+    # B*H_q partial rows of (128 + 1) floats per key split
+    n = pkg.attn_decode_workspace_bytes(4, 32, 8, 8192, 128)
+    assert n > 0 and n % (4 * 32 * 129 * 4) == 0
+    splits = n // (4 * 32 * 129 * 4)
+    assert 1 <= splits <= 8192 // 256
+    assert pkg.attn_decode_workspace_bytes(1, 8, 8, 100, 128) == 8 * 129 * 4   # one split
+    assert pkg.attn_decode_workspace_bytes(0, 8, 8, 100, 128) == -2
+    assert pkg.attn_decode_workspace_bytes(1, 12, 8, 100, 128) == -2           # H_q % H_kv
+    assert pkg.attn_decode_workspace_bytes(1, 24, 8, 100, 128) == -4           # G = 3
+    assert pkg.attn_decode_workspace_bytes(1, 8, 8, 100, 64) == -4
+    assert pkg.attn_decode_workspace_bytes(1, 8, 8, 1 << 30, 128) == -2
+
+
+def test_decode_entry_point_rejects(lib):
+    T, N, W = 0x70000000, 0x78000000, 0x80000000   # block table, seq_lens, workspace
+
+    def call(**kw):
+        a = dict(q=Q, k_cache=K, v_cache=V, block_table=T, seq_lens=N, o=O, lse=L, workspace=W,
+                 workspace_bytes=1 << 30, B=4, H_q=8, H_kv=2, d_qk=128, d_v=128, num_pages=64,
+                 page_size=64, max_pages_per_seq=16, max_seqlen=1000, softmax_scale=0.1,
+                 dtype=0, q_descale=1.0, k_descale=1.0, v_descale=1.0)
+        a.update(kw)
+        return pkg.attn_decode_paged(*a.values())
+    assert call(block_table=None) == -1
+    assert call(seq_lens=None) == -1
+    assert call(workspace=None) == -1
+    assert call(B=0) == -2
+    assert call(H_q=7) == -2                      # not a multiple of H_kv
+    assert call(H_q=48, H_kv=2) == -4            # 24 query heads per key/value head
+    assert call(page_size=48) == -2               # not a power of two
+    assert call(page_size=8) == -2
+    assert call(max_seqlen=16 * 64 + 1) == -2     # beyond the block table's pages
+    assert call(d_qk=64) == -4
+    assert call(d_v=192) == -4
+    assert call(dtype=3) == -3
+    assert call(softmax_scale=0.0) == -5
+    assert call(dtype=1, v_descale=float("inf")) == -5
+    assert call(q=Q + 8) == -6
+    assert call(block_table=T + 2) == -6
+    assert call(workspace=W + 4) == -6
+    need = pkg.attn_decode_workspace_bytes(4, 8, 2, 1000, 128)
+    assert call(workspace_bytes=need - 1) == -9
+    assert call(o=K + 64) == -7                   # o inside the key cache
+    assert call(workspace=T) == -7                # workspace over the block table
+    assert call(lse=O + 16) == -7                 # lse inside o
+
