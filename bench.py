@@ -5,7 +5,7 @@ every head), inputs resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload C4] [--gpus 1]
                   [--cpu-seconds 12] [--no-cpu] [--varlen N] [--hadamard]
-                  [--energy SECONDS]
+                  [--energy SECONDS] [--decode D1,D2,D3,D4]
 
 Workloads (seeded synthetic inputs, recipes in causal_prefill_attention_attn_amd/synth.py):
   C4  (default) FP8 e4m3, B1 H32 S32768 d128, LLM-like activations
@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--energy", type=float, default=0.0,
                     help="also run the kernel back to back for this many seconds and report "
                          "joules from the GPU's energy accumulator, average watts and TFLOP/J")
+    ap.add_argument("--decode", default="",
+                    help="also time attn_decode_paged on these decode workloads (comma "
+                         "separated names from synth.DECODE_WORKLOADS, or 'all')")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one float32 elementwise copy of this many MiB before the "
                          "warmup (reads and writes exactly that many bytes): the reference "
@@ -270,6 +273,55 @@ def energy_run(step, flops, torch, seconds):
             pass
 
 
+def time_decode(names, pkg, synth, torch, stream, steps, warmup):
+    """HBM throughput of one decode step (attn_decode_paged: the split kernel
+    and the merge kernel) per decode workload.  Algorithmic bytes: every
+    cached key and value row of every sequence once, q, o, the LSE, the
+    lengths and the block-table entries used; the partial results in the
+    workspace are the kernels' own traffic and are not counted.  Times are
+    HIP events on the launching stream around each call, inputs resident."""
+    dev = torch.device("cuda:0")
+    res = {}
+    for name in names:
+        w = synth.DECODE_WORKLOADS[name]
+        q, kc, vc, table, lens_d = synth.decode_device_inputs(w, torch, dev)
+        lens = w.seq_lens().astype(np.int64)
+        maxlen = int(lens.max())
+        esz = 2 if w.dtype == synth.BF16 else 1
+        need = pkg.attn_decode_workspace_bytes(w.B, w.H_q, w.H_kv, maxlen, w.d_v)
+        ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+        o = torch.empty((w.B, w.H_q, w.d_v), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.H_q), dtype=torch.float32, device=dev)
+
+        def call():
+            pkg.flash_attn_decode_paged(q, kc, vc, table, lens_d, maxlen, out=o, lse=lse,
+                                        workspace=ws)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        pages_used = int(((lens + w.page_size - 1) // w.page_size).sum())
+        nbytes = (int(lens.sum()) * w.H_kv * (w.d_qk + w.d_v) * esz
+                  + w.B * w.H_q * (w.d_qk * esz + w.d_v * 2 + 4) + w.B * 4 + pages_used * 4)
+        mean = float(np.mean(ms))
+        gbs = nbytes / (mean * 1e-3) / 1e9
+        res[name] = {"description": w.description, "bytes": nbytes, "ms_mean": round(mean, 4),
+                     "ms_p10_median_p90": [round(float(x), 4)
+                                           for x in np.percentile(ms, [10, 50, 90])],
+                     "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                     "workspace_bytes": need}
+        log("bench: decode %s %.4f ms %.0f GB/s" % (name, mean, gbs))
+        del q, kc, vc, ws
+    return res
+
+
 def time_hadamard(w, host, pkg, torch, stream, attn_ms, reps=10):
     """Cost of the optional Hadamard rotation, per tensor, as mean times of
     HIP events on the launching stream: the plain per-tensor quantization
@@ -418,6 +470,10 @@ def main():
     if args.energy > 0:
         log("bench: sustained run of %.0f s for energy" % args.energy)
         out["energy"] = energy_run(step, flops, torch, args.energy)
+    if args.decode:
+        names = (sorted(synth.DECODE_WORKLOADS) if args.decode == "all"
+                 else args.decode.split(","))
+        out["decode"] = time_decode(names, pkg, synth, torch, stream, args.steps, args.warmup)
     if args.hadamard:
         out["hadamard"] = time_hadamard(w, host, pkg, torch, stream, avg_kern)
     if not args.no_cpu:

@@ -110,15 +110,14 @@ __device__ __forceinline__ void e4m3_words(const uint32_t* w, int n, float* out)
   }
 }
 
-// e4m3 words -> bf16 pairs (every e4m3 value is exact in bf16), element order.
+// e4m3 words -> bf16 pairs, element order: the scaled convert with scale 1
+// (every e4m3 value is exact in bf16).
 __device__ __forceinline__ void e4m3_to_bf16_words(const uint32_t* w, int n, uint32_t* out) {
   for (int i = 0; i < n; ++i) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
-    const bf16x2 a = {(__bf16)lo[0], (__bf16)lo[1]};
-    const bf16x2 b = {(__bf16)hi[0], (__bf16)hi[1]};
-    out[2 * i] = __builtin_bit_cast(uint32_t, a);
-    out[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
+    out[2 * i] = __builtin_bit_cast(uint32_t,
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+    out[2 * i + 1] = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
   }
 }
 
@@ -257,8 +256,12 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       for (int r = 0; r < 4; ++r) sc[r][g] = __builtin_amdgcn_exp2f(sc[r][g] - mn);
       l[g] = fmaf(l[g], alpha[g], (sc[0][g] + sc[1][g]) + (sc[2][g] + sc[3][g]));
       m[g] = mn;
+      // once the running maxima settle, alpha is exactly 1 in every lane and
+      // the rescale is skipped (a multiplication by 1 changes nothing)
+      if (__any(alpha[g] != 1.0f)) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] *= alpha[g];
+        for (int e = 0; e < 8; ++e) o[g][e] *= alpha[g];
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -386,13 +389,16 @@ void launch_split_g(const DecodeArgs& a, int G, float* opart, float* lpart, floa
 }  // namespace
 
 void decode_split_policy(int64_t B, int64_t Hkv, int64_t max_seqlen, int* split, int* nsplit) {
-  // about 2048 workgroups (8 per CU) when the sequences are long enough;
-  // splits of at least 256 keys, a multiple of 64
+  // about 4096 workgroups (16 per CU) if every sequence had max_seqlen keys;
+  // splits of 256 .. 1024 keys, a multiple of 64.  The cap keeps shorter
+  // sequences of a ragged batch spread over several workgroups (workgroups
+  // past a sequence's end return at once).
   const int64_t per = B * Hkv;
-  const int64_t want = (2048 + per - 1) / per;
+  const int64_t want = (4096 + per - 1) / per;
   int64_t sp = (max_seqlen + want - 1) / want;
   sp = (sp + 63) / 64 * 64;
   if (sp < 256) sp = 256;
+  if (sp > 1024) sp = 1024;
   *split = (int)sp;
   *nsplit = (int)((max_seqlen + sp - 1) / sp);
 }

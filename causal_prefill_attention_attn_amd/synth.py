@@ -114,3 +114,79 @@ def sample_rows(S: int, n: int = 256, seed: int = 12345) -> np.ndarray:
     while len(rows) < min(n, S):
         rows.add(int(rng.integers(0, S)))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+# ------------------------------------------------------------------ decode
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: B sequences each add one query token and attend to
+    their cached keys, held in pages of page_size slots.  The 32 query heads on
+    8 key/value heads of D1-D3 are the head layout of Mistral-7B and Qwen3-8B,
+    two of the models the pages capture activations from; D4 has one
+    key/value head per query head."""
+    name: str
+    index: int
+    dtype: int
+    B: int
+    H_q: int
+    H_kv: int
+    d_qk: int
+    d_v: int
+    page_size: int
+    lengths: str        # "uniform:L" or "lognormal:median:lo:hi"
+    description: str
+
+    def seq_lens(self) -> np.ndarray:
+        kind, *a = self.lengths.split(":")
+        if kind == "uniform":
+            return np.full(self.B, int(a[0]), np.int32)
+        med, lo, hi = (int(x) for x in a)
+        rng = np.random.default_rng(np.random.PCG64(1000 * self.index + 7))
+        x = np.exp(rng.standard_normal(self.B)) * med
+        return np.clip(np.round(x), lo, hi).astype(np.int32)
+
+    def block_table(self, lens: np.ndarray):
+        """Pages of the sequences in a seeded random order over a pool with
+        no free pages: (table [B, max pages], number of pages)."""
+        need = (lens.astype(np.int64) + self.page_size - 1) // self.page_size
+        total = int(need.sum())
+        order = np.random.default_rng(np.random.PCG64(1000 * self.index + 8)).permutation(total)
+        table = np.zeros((self.B, max(int(need.max()), 1)), np.int32)
+        at = 0
+        for b, n in enumerate(need):
+            table[b, :n] = order[at:at + n]
+            at += n
+        return table, total
+
+
+DECODE_WORKLOADS = {
+    "D1": DecodeWorkload("D1", 20, BF16, 32, 32, 8, 128, 128, 64, "uniform:8192",
+                         "BF16 decode, B=32 L=8192, H_q=32 on H_kv=8, d=128, pages of 64"),
+    "D2": DecodeWorkload("D2", 21, FP8, 32, 32, 8, 128, 128, 64, "uniform:8192",
+                         "FP8 e4m3 decode, B=32 L=8192, H_q=32 on H_kv=8, d=128, pages of 64"),
+    "D3": DecodeWorkload("D3", 22, FP8, 64, 32, 8, 128, 128, 64, "lognormal:4096:64:32768",
+                         "FP8 e4m3 decode, B=64 lognormal lengths (median 4096, 64..32768), "
+                         "H_q=32 on H_kv=8, d=128, pages of 64"),
+    "D4": DecodeWorkload("D4", 23, BF16, 16, 32, 32, 128, 128, 64, "uniform:16384",
+                         "BF16 decode, B=16 L=16384, H_q=H_kv=32, d=128, pages of 64"),
+}
+
+
+def decode_device_inputs(w: DecodeWorkload, torch, device):
+    """Device tensors (q, k_cache, v_cache, block_table, seq_lens) of a decode
+    workload: N(0,1) values from a torch generator seeded with the workload
+    index (bf16, or cast to e4m3 with descale 1), lengths and pages as above."""
+    lens = w.seq_lens()
+    table, pages = w.block_table(lens)
+    g = torch.Generator(device=device)
+    g.manual_seed(1000 * w.index)
+    dt = torch.bfloat16 if w.dtype == BF16 else torch.float8_e4m3fn
+
+    def draw(shape):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dt)
+        return x if w.dtype == BF16 else x.view(torch.uint8)
+    q = draw((w.B, w.H_q, w.d_qk))
+    kc = draw((pages, w.page_size, w.H_kv, w.d_qk))
+    vc = draw((pages, w.page_size, w.H_kv, w.d_v))
+    return (q, kc, vc, torch.from_numpy(table).to(device),
+            torch.from_numpy(lens).to(device))
