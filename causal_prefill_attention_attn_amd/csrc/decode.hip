@@ -156,6 +156,15 @@ __device__ __forceinline__ void row_values(const RowPart<DQK, kFP8>& r, float* o
   }
 }
 
+// Tiles each wave keeps in flight beyond the one it works on: chosen so that
+// the ring of tile buffers (16 registers per e4m3 tile, 32 per bf16 tile)
+// leaves the kernel's occupancy where it was with one tile ahead.
+template <bool kFP8, int G>
+constexpr int prefetch_tiles() {
+  if (kFP8) return G <= 4 ? 3 : 1;
+  return G <= 2 ? 2 : 1;
+}
+
 template <int DQK, int G, bool kFP8>
 __global__ void __launch_bounds__(64 * kWaves)
 decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
@@ -223,18 +232,14 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     for (int e = 0; e < 8; ++e) o[g][e] = 0.0f;
   }
 
-  int t = wave;
-  Tile cur;
-  if (t < ntile) cur = load_tile(t);
-  for (; t < ntile; t += kWaves) {
-    Tile nxt = cur;
-    if (t + kWaves < ntile) nxt = load_tile(t + kWaves);
+  // one tile: scores, online softmax update, P.V
+  auto process = [&](const Tile& x, int t) {
     const int key0 = k0 + t * kTile;
     float sc[4][G];  // logits in log2 units, then probabilities
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool valid = key0 + 4 * r + grp < k1;
-      const QP kp = row_pairs<DQK, kFP8>(cur.k[r]);
+      const QP kp = row_pairs<DQK, kFP8>(x.k[r]);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float acc = 0.0f;
@@ -256,23 +261,43 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       for (int r = 0; r < 4; ++r) sc[r][g] = __builtin_amdgcn_exp2f(sc[r][g] - mn);
       l[g] = fmaf(l[g], alpha[g], (sc[0][g] + sc[1][g]) + (sc[2][g] + sc[3][g]));
       m[g] = mn;
-      // once the running maxima settle, alpha is exactly 1 in every lane and
-      // the rescale is skipped (a multiplication by 1 changes nothing)
-      if (__any(alpha[g] != 1.0f)) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] *= alpha[g];
-      }
+      for (int e = 0; e < 8; ++e) o[g][e] *= alpha[g];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float vv[8];
-      row_values<128, kFP8>(cur.v[r], vv);
+      row_values<128, kFP8>(x.v[r], vv);
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[g][e] = fmaf(sc[r][g], vv[e], o[g][e]);
     }
-    cur = nxt;
+  };
+
+  // Ring of kAhead + 1 tile buffers in registers, indexed at compile time
+  // (the loop is unrolled by the ring size): while tile t is processed,
+  // tiles t+4 .. t+4*kAhead are in flight.  The body has no condition, so the
+  // compiler's count of outstanding loads stays exact: the wave's tile count
+  // is rounded up to whole rings, loads past the last tile reload it (a cache
+  // hit) and tiles past the last one are processed fully masked, which
+  // leaves m, l and o unchanged (alpha = 1, p = 0).
+  constexpr int kAhead = prefetch_tiles<kFP8, G>();
+  constexpr int kRing = kAhead + 1;
+  const int nmine = wave < ntile ? (ntile - wave + kWaves - 1) / kWaves : 0;
+  Tile ring[kRing];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) ring[i] = load_tile(min(wave + kWaves * i, ntile - 1));
+  for (int it = 0; it < nmine; it += kRing) {
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      const int t = wave + kWaves * (it + j);
+      ring[(j + kAhead) % kRing] = load_tile(min(t + kWaves * kAhead, ntile - 1));
+      process(ring[j], t);
+      // keep each step's loads in its own step: hoisting later loads only
+      // lengthens register live ranges
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // merge the four lane groups of the wave (lanes sub, sub+16, sub+32, sub+48
@@ -350,9 +375,13 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
     if (lse != nullptr && d == 0) lse[bh] = -INFINITY;
     return;
   }
+  // unrolled so that the loads of several splits are in flight together;
+  // the sums still run in split order
   float M = lp[0];
+#pragma unroll 8
   for (int s = 1; s < ns; ++s) M = fmaxf(M, lp[s]);
   float wsum = 0.0f, acc = 0.0f;
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) {
     const float w = expf(lp[s] - M);
     wsum += w;
