@@ -322,11 +322,12 @@ def time_decode(names, pkg, synth, torch, stream, steps, warmup):
     return res
 
 
-def time_hadamard(w, host, pkg, torch, stream, attn_ms, reps=10):
+def time_hadamard(w, host, pkg, torch, stream, attn_ms, dev_in, ds, reps=10):
     """Cost of the optional Hadamard rotation, per tensor, as mean times of
     HIP events on the launching stream: the plain per-tensor quantization
     (amax pass + encode pass) of Q, K, V against the fused rotate+quantize
-    passes, and the standalone rotation of O (bf16) that undoes a rotated V.
+    passes, the standalone rotation of O (bf16) that undoes a rotated V, and
+    the attention itself with that O rotation fused into its epilogue (FP8).
     Rates count one read of the input per pass and one write of the codes."""
     dev = torch.device("cuda:0")
 
@@ -366,7 +367,19 @@ def time_hadamard(w, host, pkg, torch, stream, attn_ms, reps=10):
     res["o_rotate_GB/s"] = round(2 * o.numel() * 2 / (orot * 1e-3) / 1e9, 1)
     res["added_ms"] = round(extra + orot, 4)
     res["added_frac_of_attention"] = round((extra + orot) / attn_ms, 4)
+    from causal_prefill_attention_attn_amd import synth
+    if w.dtype == synth.FP8:
+        def attn(rot):
+            return lambda: pkg.flash_attn_func(*dev_in, softmax_scale=w.softmax_scale,
+                                               causal=True, q_descale=ds[0], k_descale=ds[1],
+                                               v_descale=ds[2], out=y, hadamard_o=rot)
+        plain_ms, fused_ms = timed(attn(False)), timed(attn(True))
+        res["attention_ms"] = round(plain_ms, 4)
+        res["attention_with_fused_o_rotation_ms"] = round(fused_ms, 4)
+        res["added_ms_with_fused_o_rotation"] = round(extra + fused_ms - plain_ms, 4)
+        res["added_frac_with_fused_o_rotation"] = round((extra + fused_ms - plain_ms) / plain_ms, 4)
     return res
+
 
 
 def main():
@@ -475,7 +488,7 @@ def main():
                  else args.decode.split(","))
         out["decode"] = time_decode(names, pkg, synth, torch, stream, args.steps, args.warmup)
     if args.hadamard:
-        out["hadamard"] = time_hadamard(w, host, pkg, torch, stream, avg_kern)
+        out["hadamard"] = time_hadamard(w, host, pkg, torch, stream, avg_kern, t, ds)
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, synth)

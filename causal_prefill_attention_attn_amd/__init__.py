@@ -19,7 +19,7 @@ import os
 
 __all__ = [
     "ATTN_DTYPE_BF16", "ATTN_DTYPE_FP8", "AttnError", "lib_path", "load_library",
-    "attn_fwd", "attn_fwd_varlen", "attn_amax_f32", "attn_quantize_e4m3", "attn_status_string",
+    "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_amax_f32", "attn_quantize_e4m3", "attn_status_string",
     "attn_version", "attn_hadamard_f32", "attn_hadamard_bf16", "attn_hadamard_amax_f32",
     "attn_hadamard_quantize_e4m3", "attn_decode_paged", "attn_decode_workspace_bytes",
     "flash_attn_func", "flash_attn_varlen_func", "flash_attn_decode_paged", "quantize_fp8",
@@ -63,6 +63,9 @@ def load_library():
     lib.attn_fwd.restype = i32
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32,
                              f32, f32, f32, vp]
+    lib.attn_fwd_ex.restype = i32
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32,
+                                f32, f32, f32, ctypes.c_uint32, vp]
     lib.attn_fwd_varlen.restype = i32
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32,
                                     i32, i32, f32, f32, f32, vp]
@@ -101,6 +104,13 @@ def attn_fwd(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale, causal, dtype,
     """Direct call of the C function on integer addresses; returns the status."""
     return int(load_library().attn_fwd(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale,
                                        causal, dtype, q_descale, k_descale, v_descale, stream))
+
+
+def attn_fwd_ex(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale, causal, dtype,
+                q_descale=1.0, k_descale=1.0, v_descale=1.0, flags=0, stream=None) -> int:
+    return int(load_library().attn_fwd_ex(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale,
+                                          causal, dtype, q_descale, k_descale, v_descale, flags,
+                                          stream))
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, n_seqs, total, max_seqlen, H, d_qk, d_v,
@@ -176,13 +186,15 @@ def _element_dtype(t) -> int:
 
 
 def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_descale=1.0,
-                    v_descale=1.0, out=None, lse=None, return_lse=True):
+                    v_descale=1.0, out=None, lse=None, return_lse=True, hadamard_o=False):
     """Forward attention on [B, S, H, D] tensors.
 
     q, k: [B, S, H, d_qk]; v: [B, S, H, d_v]; all bfloat16, or all FP8 e4m3
     (``torch.float8_e4m3fn`` or uint8 codes) with per-tensor descales.
-    Returns ``(o, lse)``: o bfloat16 [B, S, H, d_v], lse float32 [B, H, S]
-    (natural log); lse is None when ``return_lse`` is False.
+    ``hadamard_o`` (FP8): rows of O are multiplied by the normalised Hadamard
+    matrix, undoing a V rotated before quantization (``quantize_fp8(v,
+    rotate=True)``).  Returns ``(o, lse)``: o bfloat16 [B, S, H, d_v], lse
+    float32 [B, H, S] (natural log); lse is None when ``return_lse`` is False.
     """
     torch = _torch()
     dt = _element_dtype(q)
@@ -204,11 +216,12 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_d
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     if not return_lse:
         lse = None
-    st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                  lse.data_ptr() if lse is not None else None, B, S, H, d_qk, d_v,
-                  float(softmax_scale), int(bool(causal)), dt, float(q_descale),
-                  float(k_descale), float(v_descale), _stream_handle(q.device))
-    _check(st, "attn_fwd")
+    st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                     lse.data_ptr() if lse is not None else None, B, S, H, d_qk, d_v,
+                     float(softmax_scale), int(bool(causal)), dt, float(q_descale),
+                     float(k_descale), float(v_descale), 1 if hadamard_o else 0,
+                     _stream_handle(q.device))
+    _check(st, "attn_fwd_ex")
     return out, lse
 
 

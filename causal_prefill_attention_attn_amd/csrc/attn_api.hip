@@ -51,7 +51,8 @@ namespace {
 // S the longest, total rows).
 int fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu,
         int64_t total, int64_t B, int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale,
-        int causal, int dtype, float q_descale, float k_descale, float v_descale, void* stream) {
+        int causal, int dtype, float q_descale, float k_descale, float v_descale, unsigned flags,
+        void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B < 1 || S < 1 || H < 1 || total < 1) return ATTN_ERR_SHAPE;
   // 32-bit indices inside the kernels: rows, heads, problem*head and the grid
@@ -61,6 +62,9 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, const 
   if (nqb * B * H > INT32_MAX) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8) return ATTN_ERR_DTYPE;
   if (!((d_qk == 128 || d_qk == 192) && d_v == 128) || (causal != 0 && causal != 1))
+    return ATTN_ERR_UNSUPPORTED;
+  if ((flags & ~ATTN_FLAG_HADAMARD_O) != 0 ||
+      ((flags & ATTN_FLAG_HADAMARD_O) && dtype != ATTN_DTYPE_FP8))
     return ATTN_ERR_UNSUPPORTED;
   if (!finite_positive(softmax_scale)) return ATTN_ERR_SCALE;
   if (dtype == ATTN_DTYPE_FP8 &&
@@ -90,7 +94,8 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, const 
                                   softmax_scale, causal, st);
   else
     rc = cpattn::launch_attn_fp8(q, k, v, o, lse, cu, total, (int)B, (int)S, (int)H, d_qk,
-                                 softmax_scale, causal, q_descale, k_descale, v_descale, st);
+                                 softmax_scale, causal, q_descale, k_descale, v_descale,
+                                 (flags & ATTN_FLAG_HADAMARD_O) != 0, st);
   return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -103,7 +108,16 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              float q_descale, float k_descale, float v_descale, void* stream) {
   if (B >= 1 && S >= 1 && B > INT64_MAX / S) return ATTN_ERR_SHAPE;
   return fwd(q, k, v, o, lse, nullptr, B >= 1 && S >= 1 ? B * S : 0, B, S, H, d_qk, d_v,
-             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, stream);
+             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, 0u, stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale, int causal,
+                int dtype, float q_descale, float k_descale, float v_descale, unsigned flags,
+                void* stream) {
+  if (B >= 1 && S >= 1 && B > INT64_MAX / S) return ATTN_ERR_SHAPE;
+  return fwd(q, k, v, o, lse, nullptr, B >= 1 && S >= 1 ? B * S : 0, B, S, H, d_qk, d_v,
+             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, flags, stream);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -112,7 +126,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     float q_descale, float k_descale, float v_descale, void* stream) {
   if (!cu_seqlens) return ATTN_ERR_NULL;
   return fwd(q, k, v, o, lse, cu_seqlens, total, n_seqs, max_seqlen, H, d_qk, d_v,
-             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, stream);
+             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, 0u, stream);
 }
 
 int attn_amax_f32(const float* x, int64_t n, float* amax_out, void* stream) {

@@ -114,6 +114,51 @@ struct Layout {
   __device__ static int k_swz(int row) { return DQK == 128 ? (row >> 1) & 7 : row & 15; }
 };
 
+// O rows times the Sylvester-Hadamard matrix of order 128 (unnormalised),
+// in place.  Undoes a V rotated by the normalised matrix before quantization
+// (the rotation of "Precisao, estabilidade e efeito na pratica" on the
+// miraibroadcast.com page): (P.(V H)) H = P.V since H H = 128 I.  Lane
+// (col, half) holds element j = d*32 + g*8 + half*4 + e of row col at
+// oacc[d][g*4 + e]; the butterfly on bit b of j pairs (x_j, x_{j+2^b}) into
+// (x_j + x_{j+2^b}, x_j - x_{j+2^b}).  Bits 0, 1, 3, 4, 5, 6 are inside the
+// lane; bit 2 is the lane half, exchanged by a permlane32 swap.
+__device__ __forceinline__ void hadamard_o_rows(f32x16* oacc, int half) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1)  // bits of g*4 + e
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!(i & m)) {
+          const float a = oacc[d][i], b = oacc[d][i | m];
+          oacc[d][i] = a + b;
+          oacc[d][i | m] = a - b;
+        }
+#pragma unroll
+  for (int m = 1; m < 4; m <<= 1)  // bits of d
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      if (!(d & m)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float a = oacc[d][i], b = oacc[d | m][i];
+          oacc[d][i] = a + b;
+          oacc[d | m][i] = a - b;
+        }
+      }
+  // bit 2 of j: the swap leaves the lower-half lane's value in r[0] and the
+  // upper-half lane's in r[1] in every lane
+  const float sgn = half ? -1.0f : 1.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(oacc[d][i]),
+                                                      __float_as_uint(oacc[d][i]), false, false);
+      oacc[d][i] = __builtin_fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
+    }
+}
+
 template <int DQK, int BN>
 struct Smem {
   using L = Layout<DQK, BN>;
@@ -137,7 +182,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
                     const uint8_t* __restrict__ v, __bf16* __restrict__ o,
                     float* __restrict__ lse, const int32_t* __restrict__ cu, int64_t total,
                     int S_max, int H, int BH, int nqb, float c_log2,
-                    float v_descale, int causal, float lazy_log2) {
+                    float v_descale, int causal, float lazy_log2, int rot_o) {
   using LY = Layout<DQK, BN>;
   constexpr int kWaves = 4 * kOcc;
   constexpr int kBM = 32 * kWaves;                 // query rows per workgroup
@@ -367,10 +412,12 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   }
 
   // ---- epilogue
+  if (rot_o) hadamard_o_rows(oacc, half);
   const float l_tot = lacc[0];
   const int qi = q0w + col;
   if (qi < S) {
-    const float inv = v_descale / l_tot;
+    // 1/sqrt(128) normalises the rotation
+    const float inv = v_descale / l_tot * (rot_o ? 0.08838834764831845f : 1.0f);
     __bf16* orow = o + ((sr.row0 + qi) * H + h) * kDV;
 #pragma unroll
     for (int d = 0; d < kDV / 32; ++d)
@@ -391,7 +438,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
 int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
                     float softmax_scale, int causal, float q_descale, float k_descale,
-                    float v_descale, hipStream_t stream) {
+                    float v_descale, bool rot_o, hipStream_t stream) {
   const int occ = 2;                      // waves per SIMD (register budget)
   const int bm = 128 * occ;               // query rows per workgroup
   const int nqb = (S + bm - 1) / bm;
@@ -412,7 +459,7 @@ int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float*
 #define CPATTN_LAUNCH_FP8(DQK, BN, LEAN, OCC)                                                     \
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, BN, LEAN, OCC>), grid, dim3(256 * OCC), 0, stream, \
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, cu, \
-                     total, S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2)
+                     total, S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2, (int)rot_o)
   if (d_qk == 128) {
     if (lean) CPATTN_LAUNCH_FP8(128, 64, true, 2);
     else CPATTN_LAUNCH_FP8(128, 64, false, 2);

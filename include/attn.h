@@ -49,6 +49,9 @@ extern "C" {
 #define ATTN_ERR_LAUNCH (-8)      /* the HIP runtime rejected the kernel launch */
 #define ATTN_ERR_WORKSPACE (-9)   /* workspace smaller than attn_decode_workspace_bytes */
 
+/* flags of attn_fwd_ex */
+#define ATTN_FLAG_HADAMARD_O 1u /* O rows times the normalised Hadamard matrix (FP8 only) */
+
 /* element types of q, k, v */
 #define ATTN_DTYPE_BF16 0 /* bfloat16 */
 #define ATTN_DTYPE_FP8 1  /* OCP FP8 E4M3FN (bias 7, max 448, no inf) */
@@ -100,6 +103,24 @@ const char* attn_status_string(int status);
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
              int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale, int causal, int dtype,
              float q_descale, float k_descale, float v_descale, void* stream);
+
+/*
+ * attn_fwd_ex -- attn_fwd with option flags.
+ *   flags  0, or ATTN_FLAG_HADAMARD_O: each row of O (d_v = 128 values) is
+ *          multiplied by the normalised Sylvester-Hadamard matrix of order
+ *          128 before it is rounded to bf16.  This undoes a V whose rows were
+ *          rotated by that matrix before FP8 quantization (attn_hadamard_*),
+ *          the rotation that "Precisao, estabilidade e efeito na pratica" on
+ *          the miraibroadcast.com page credits with about half of the FP8
+ *          error, without a separate pass over O.  FP8 only.
+ * Every other argument, check and return code is that of attn_fwd; unknown
+ * flag bits, or ATTN_FLAG_HADAMARD_O with BF16, return ATTN_ERR_UNSUPPORTED.
+ * With flags = 0 the results equal those of attn_fwd bit for bit.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale, int causal,
+                int dtype, float q_descale, float k_descale, float v_descale, unsigned flags,
+                void* stream);
 
 /*
  * attn_fwd_varlen -- attn_fwd over a batch of sequences of different

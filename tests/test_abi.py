@@ -32,7 +32,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    assert names == sorted(["attn_version", "attn_status_string", "attn_fwd", "attn_fwd_varlen",
+    assert names == sorted(["attn_version", "attn_status_string", "attn_fwd", "attn_fwd_ex",
+                            "attn_fwd_varlen",
                             "attn_amax_f32",
                             "attn_quantize_e4m3", "attn_hadamard_f32", "attn_hadamard_bf16",
                             "attn_hadamard_amax_f32", "attn_hadamard_quantize_e4m3",
@@ -188,4 +189,18 @@ def test_decode_entry_point_rejects(lib):
     assert call(o=K + 64) == -7                   # o inside the key cache
     assert call(workspace=T) == -7                # workspace over the block table
     assert call(lse=O + 16) == -7                 # lse inside o
+
+
+def test_fwd_ex_flags(lib):
+    def call(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, S=256, H=2, d_qk=128, d_v=128,
+                 softmax_scale=0.1, causal=1, dtype=1, q_descale=1.0, k_descale=1.0,
+                 v_descale=1.0, flags=0)
+        a.update(kw)
+        return pkg.attn_fwd_ex(*a.values())
+    assert call(flags=2) == -4                   # unknown flag bit
+    assert call(flags=1, dtype=0) == -4          # the O rotation is FP8 only
+    assert call(flags=1, q=None) == -1
+    assert call(flags=1, B=0) == -2
+    assert call(flags=1, o=Q + 64) == -7
 

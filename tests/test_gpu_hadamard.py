@@ -23,7 +23,7 @@ import torch
 
 import causal_prefill_attention_attn_amd as pkg
 from causal_prefill_attention_attn_amd import synth
-from gpu_util import DEV, TOL, LSE_REL, WORST_ROW, errors, o_to_f64
+from gpu_util import DEV, TOL, LSE_REL, WORST_ROW, errors, o_to_f64, u8_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +158,78 @@ def test_fused_rotation_quantization(oracle, d):
     diff = np.abs(got - ref)
     print("fused rotate+quantize d%d: %d of %d codes differ from the oracle's" % (d, int((diff > 0).sum()), diff.size))
     assert diff.max() <= 1 and (diff > 0).mean() <= 1e-3
+
+
+def _gpu_fp8_fused(xs, tau):
+    """Rotate and quantize Q, K, V; attention with the O rotation fused into
+    the kernel's epilogue (attn_fwd_ex with ATTN_FLAG_HADAMARD_O)."""
+    t = [torch.from_numpy(x).to(DEV) for x in xs]
+    codes, ds = zip(*[pkg.quantize_fp8(x, rotate=True) for x in t])
+    o, lse = pkg.flash_attn_func(*codes, softmax_scale=tau, causal=True, q_descale=ds[0],
+                                 k_descale=ds[1], v_descale=ds[2], hadamard_o=True)
+    torch.cuda.synchronize()
+    return o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("d_qk", [128, 192])
+def test_fused_o_rotation_matches_oracle(oracle, d_qk):
+    S, H = 700, 2
+    tau = 1.0 / np.sqrt(d_qk)
+    xs = _inputs(S, H, d_qk, 4, 4242 + d_qk, shared=False, scale=5.0)
+    go, gl = _gpu_fp8_fused(xs, tau)
+    ro, rl = _oracle_fp8(oracle, xs, True, tau)
+    pooled, rms, worst = errors(go, ro)
+    tol = TOL[synth.FP8]
+    msg = "fused O rotation d%d pooled %.3e row-RMS %.3e worst %.3e max|dlse| %.3e" % (
+        d_qk, pooled, rms, worst, float(np.abs(gl - rl).max()))
+    print(msg)
+    assert pooled <= tol and rms <= tol and worst <= WORST_ROW[synth.FP8] * tol, msg
+    assert float((np.abs(gl - rl) - LSE_REL[synth.FP8] * np.abs(rl)).max()) <= tol, msg
+    # against the separate bf16 pass over O: the fused path rounds once, the
+    # separate one twice, so they agree to a few bf16 units
+    so, sl = _gpu_fp8(xs, True, tau)
+    assert np.array_equal(sl, gl)
+    assert float(np.linalg.norm(so - go) / np.linalg.norm(go)) <= 8e-3
+
+
+def test_fused_o_rotation_of_constant_values_is_the_hadamard_row(oracle):
+    """Every V row equal to u makes O = u in every row (the softmax weights sum
+    to one), so the fused output must be u.H for every query row and head:
+    this fixes the rotation's element order and signs."""
+    rng = np.random.default_rng(77)
+    S, H, d = 300, 2, 128
+    q = rng.standard_normal((1, S, H, d)).astype(np.float32)
+    k = rng.standard_normal((1, S, H, d)).astype(np.float32)
+    u = rng.standard_normal(128).astype(np.float32)
+    v = np.broadcast_to(u, (1, S, H, 128)).copy()
+    dq, dk, dv = (oracle.descale_amax(x) for x in (q, k, v))
+    enc = [oracle.quantize_e4m3(x, dd) for x, dd in zip((q, k, v), (dq, dk, dv))]
+    dev = [u8_to_device(x) for x in enc]
+    o, _ = pkg.flash_attn_func(*dev, softmax_scale=0.1, causal=True, q_descale=dq, k_descale=dk,
+                               v_descale=dv, hadamard_o=True)
+    torch.cuda.synchronize()
+    go = o_to_f64(o)
+    uh = oracle.hadamard(oracle.decode_e4m3(enc[2][0, 0, 0]) * dv)
+    err = np.abs(go - uh).max() / np.abs(uh).max()
+    print("constant-V rotation max error %.3e" % err)
+    # the e4m3 rounding of P cancels in sum(p u) / sum(p): what is left is the
+    # bf16 rounding of O, at most 2^-8 of the largest element
+    assert err <= 5e-3
+
+
+def test_fwd_ex_without_flags_equals_fwd_bitwise(oracle):
+    rng = np.random.default_rng(5)
+    xs = [rng.standard_normal((1, 400, 2, 128)).astype(np.float32) for _ in range(3)]
+    ds = [oracle.descale_amax(x) for x in xs]
+    dev = [u8_to_device(oracle.quantize_e4m3(x, dd)) for x, dd in zip(xs, ds)]
+    outs = []
+    for ex in (False, True):
+        o = torch.empty((1, 400, 2, 128), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((1, 2, 400), dtype=torch.float32, device=DEV)
+        args = [t.data_ptr() for t in dev] + [o.data_ptr(), lse.data_ptr(), 1, 400, 2, 128, 128,
+                                              0.09, 1, 1, ds[0], ds[1], ds[2]]
+        st = pkg.attn_fwd_ex(*args, 0) if ex else pkg.attn_fwd(*args)
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append((o.view(torch.int16).clone(), lse.view(torch.int32).clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
