@@ -307,6 +307,26 @@ def time_decode(names, pkg, synth, torch, stream, steps, warmup):
             b.record(stream)
         torch.cuda.synchronize()
         ms = [a.elapsed_time(b) for a, b in ev]
+        # the same step captured in a HIP graph (10 calls per replay): what a
+        # serving loop that replays graphs would see, launch overhead removed
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for _ in range(10):
+                    call()
+        torch.cuda.current_stream().wait_stream(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        for _ in range(max(1, steps // 10)):
+            g.replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = ga.elapsed_time(gb) / (10 * max(1, steps // 10))
+        del g
         pages_used = int(((lens + w.page_size - 1) // w.page_size).sum())
         nbytes = (int(lens.sum()) * w.H_kv * (w.d_qk + w.d_v) * esz
                   + w.B * w.H_q * (w.d_qk * esz + w.d_v * 2 + 4) + w.B * 4 + pages_used * 4)
@@ -316,6 +336,8 @@ def time_decode(names, pkg, synth, torch, stream, steps, warmup):
                      "ms_p10_median_p90": [round(float(x), 4)
                                            for x in np.percentile(ms, [10, 50, 90])],
                      "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                     "graph_ms_per_step": round(graph_ms, 4),
+                     "graph_GB/s": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
                      "workspace_bytes": need}
         log("bench: decode %s %.4f ms %.0f GB/s" % (name, mean, gbs))
         del q, kc, vc, ws
