@@ -97,6 +97,25 @@ __device__ __forceinline__ i16x4 ds_read_tr16(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
   return r;
 }
+// ds_read_b64_tr_b8 as inline assembly, for the same reason: lanes 2r and
+// 2r+1 of a 16-lane group supply row r (16 bytes) and lane i receives byte
+// i of every row (eight rows).  Order its result with lds_wait4() before use.
+template <int OFF>
+__device__ __forceinline__ i32x2 ds_read_tr8(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+// s_waitcnt lgkmcnt(N) tied to the four registers pairs of a transposed
+// operand read, so that nothing that reads them (including the moves that
+// assemble the operand) can be placed above the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait4(i32x2& a, i32x2& b, i32x2& c, i32x2& d) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
+
 // s_waitcnt lgkmcnt(N), tied to one operand register set so that its uses
 // cannot be scheduled above it.  LDS operations complete in order, so with
 // at most N of them (and any scalar loads) still in flight every older LDS

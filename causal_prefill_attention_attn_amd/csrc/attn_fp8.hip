@@ -317,7 +317,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   for (int t = 0; t < 3; ++t)
     if (t < nkt) issue_tile(t);
   if (nkt > 2) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
-  __syncthreads();
+  barrier_nofence();
   if (active(0)) qk(0, sa);
 
   auto step = [&](int t, f32x16* scur, f32x16* snext) {
@@ -338,9 +338,14 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
             scur[kb][i] = kofs > lim ? -INFINITY : scur[kb][i];
           }
       }
-      float mx = -INFINITY;
+      // two chains of three-input maxima (16 v_max3 for 32 scores)
+      float mx0 = fmaxf(scur[0][0], scur[1][0]), mx1 = fmaxf(scur[0][1], scur[1][1]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(scur[0][i], scur[1][i]));
+      for (int i = 2; i < 16; i += 2) {
+        mx0 = fmaxf(fmaxf(mx0, scur[0][i]), scur[1][i]);
+        mx1 = fmaxf(fmaxf(mx1, scur[0][i + 1]), scur[1][i + 1]);
+      }
+      const float mx = fmaxf(mx0, mx1);
       const float bmax = pair_max(mx) * c_log2;
       if (__any(bmax > m_run + lazy_log2)) {
         const float m_new = fmaxf(m_run, bmax);
@@ -386,24 +391,37 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
         }
       }
       // ---- O^T += V^T . P^T and l += ones . P^T
-      const uint8_t* vt = sm.v[t % LY::kStages];
+      // V^T operands of the four 32-row blocks of d, read two blocks ahead
+      // (inline assembly: the reads wait for no buffer-to-LDS load in flight)
+      const uint32_t vt = lds_addr(sm.v[t % LY::kStages]);
+      i32x2 r[2][4];
+      auto vread = [&](int d, i32x2* x) {
+        const uint32_t a = vt + (vbase ^ (d << 5));
+        x[0] = ds_read_tr8<0 * 16 * kDV>(a);
+        x[1] = ds_read_tr8<1 * 16 * kDV>(a);
+        x[2] = ds_read_tr8<2 * 16 * kDV>(a);
+        x[3] = ds_read_tr8<3 * 16 * kDV>(a);
+      };
+      vread(0, r[0]);
+      vread(1, r[1]);
 #pragma unroll
       for (int d = 0; d < kDV / 32; ++d) {
-        i32x2 r[4];
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
-          r[t4] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2*)(vt + t4 * 16 * kDV + (vbase ^ (d << 5))));
+        i32x2* x = r[d & 1];
+        if (d + 1 < kDV / 32) lds_wait4<4>(x[0], x[1], x[2], x[3]);  // block d+1 may be in flight
+        else lds_wait4<0>(x[0], x[1], x[2], x[3]);
         const i32x8 a = __builtin_shufflevector(
-            __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3),
-            __builtin_shufflevector(r[2], r[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+            __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3),
+            __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
+        if (d + 2 < kDV / 32) vread(d + 2, x);
       }
       lacc = mfma_f8(ones, pw, lacc, kE8M0One, pscale);
     }
-    // tile t+2 must be complete for S(t+2) in the next iteration
+    // tile t+2 must be complete for S(t+2) in the next iteration: each wave
+    // waits for its own loads of it, then the barrier (no fence: a release
+    // would wait for the loads of tile t+3 as well)
     if (more) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
-    __syncthreads();
+    barrier_nofence();
   };
   // unrolled by two so that the two score buffers swap roles without copies
   for (int t = 0; t < nkt; t += 2) {
