@@ -246,14 +246,15 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             scur[kb][i] = kofs > lim ? -INFINITY : scur[kb][i];
           }
       }
-      // row max: two chains of three-input maxima
+      // row max: two chains of three-input maxima (max(max(m, a), b) is one
+      // v_max3; max(m, max(a, b)) was compiled as two instructions)
       float ma = -INFINITY, mb = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 4) {
-          ma = fmaxf(ma, fmaxf(scur[kb][i], scur[kb][i + 1]));
-          mb = fmaxf(mb, fmaxf(scur[kb][i + 2], scur[kb][i + 3]));
+          ma = fmaxf(fmaxf(ma, scur[kb][i]), scur[kb][i + 1]);
+          mb = fmaxf(fmaxf(mb, scur[kb][i + 2]), scur[kb][i + 3]);
         }
       const float tmax = pair_max(fmaxf(ma, mb)) * c_log2;
       if (__any(tmax > m_run)) {
