@@ -49,9 +49,10 @@ def parse():
     ap.add_argument("--varlen", type=int, default=0,
                     help="also time attn_fwd_varlen on the workload's tokens split into this "
                          "many packed sequences of seeded random lengths")
-    ap.add_argument("--energy", type=float, default=0.0,
-                    help="also run the kernel back to back for this many seconds and report "
-                         "joules from the GPU's energy accumulator, average watts and TFLOP/J")
+    ap.add_argument("--energy", type=float, default=6.0,
+                    help="run the kernel back to back for this many seconds (0: skip) and report "
+                         "joules from the GPU's energy accumulator, average watts, TFLOP/J and "
+                         "the shader clock sampled meanwhile (median, p10)")
     ap.add_argument("--decode", default="",
                     help="also time attn_decode_paged on these decode workloads (comma "
                          "separated names from synth.DECODE_WORKLOADS, or 'all')")
@@ -85,12 +86,12 @@ def device_inputs(w, torch, pkg, synth):
 def profiled(w, dtname):
     """Figures rocprofv3 measured for this workload's kernel, from profiles/:
     HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known
-    size) and the sustained shader clock (GRBM_GUI_ACTIVE / duration).  Both
-    None when no summary exists or the kernel source changed since it was
-    taken."""
+    size), the sustained shader clock (GRBM_GUI_ACTIVE / duration) and the
+    MFMA-busy and VALU-busy fractions.  All None when no summary exists or
+    the kernel source changed since it was taken."""
     import hashlib
     import re
-    none = {"traffic": None, "sclk_mhz": None}
+    none = {"traffic": None, "sclk_mhz": None, "mfma_busy": None, "valu_busy": None}
     path = os.path.join(ROOT, "profiles", "attn_fwd_%s_d%d_%s.md" % (dtname, w.d_qk, w.name))
     if not os.path.exists(path):
         return none
@@ -103,6 +104,9 @@ def profiled(w, dtname):
         m = re.search(r"sustained clock .*: (\d+) MHz", line)
         if m:
             fields["sclk_mhz"] = m.group(1)
+        m = re.match(r"- (MFMA|VALU) busy = .*: ([0-9.]+)%", line)
+        if m:
+            fields[m.group(1).lower() + "_busy"] = float(m.group(2)) / 100.0
     try:
         src = open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()
     except (KeyError, OSError):
@@ -110,7 +114,8 @@ def profiled(w, dtname):
     if hashlib.sha256(src).hexdigest() != fields.get("kernel_source_sha256"):
         return none
     return {"traffic": int(fields["traffic_bytes_per_launch"]),
-            "sclk_mhz": int(fields["sclk_mhz"]) if "sclk_mhz" in fields else None}
+            "sclk_mhz": int(fields["sclk_mhz"]) if "sclk_mhz" in fields else None,
+            "mfma_busy": fields.get("mfma_busy"), "valu_busy": fields.get("valu_busy")}
 
 
 def input_stats(w, host, nrows=64):
@@ -224,46 +229,67 @@ def energy_run(step, flops, torch, seconds):
         h = match[0]
 
         def joules():
+            """(joules, counter timestamp): the accumulator is updated in
+            steps, so power is its difference over the difference of the
+            timestamps it carries, not over host time"""
             c = amdsmi.amdsmi_get_energy_count(h)
-            return c["energy_accumulator"] * c["counter_resolution"] * 1e-6
+            return c["energy_accumulator"] * c["counter_resolution"] * 1e-6, c["timestamp"]
 
-        # time one launch to size the loop
+        # time one launch to size the loop, then run unmeasured for a while:
+        # board power and clock take about a second to settle
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         step()
         torch.cuda.synchronize()
         per = max(time.perf_counter() - t0, 1e-4)
+        warm = max(1.0, seconds / 3.0)
+        for i in range(max(1, int(warm / per))):
+            step()
+            if i % 64 == 63:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
         n = max(10, int(seconds / per))
-        watts, mhz = [], []
+        watts_s, mhz = [], []
 
         def sample():  # while launches are queued, so the GPU is busy
             try:
                 p = amdsmi.amdsmi_get_power_info(h).get("current_socket_power")
                 if isinstance(p, (int, float)):
-                    watts.append(p)
+                    watts_s.append(p)
                 c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
                 if isinstance(c, (int, float)):
                     mhz.append(c)
             except Exception:
                 pass
 
-        e0, t0 = joules(), time.perf_counter()
+        (e0, c0), t0 = joules(), time.perf_counter()
         for i in range(n):
             step()
-            if i % 64 == 31:
+            if i % 16 == 8:
                 sample()
             if i % 64 == 63:
                 torch.cuda.synchronize()  # keep the launch queue short
         torch.cuda.synchronize()
-        e1, t1 = joules(), time.perf_counter()
+        (e1, c1), t1 = joules(), time.perf_counter()
         j, sec = e1 - e0, t1 - t0
-        return {"launches": n, "seconds": round(sec, 3), "joules": round(j, 2),
-                "avg_watts": round(j / sec, 1) if sec > 0 else None,
-                "TFLOP/s": round(flops * n / sec / 1e12, 1),
-                "TFLOP/J": round(flops * n / j / 1e12, 3) if j > 0 else None,
-                "socket_watts_sampled_median": float(np.median(watts)) if watts else None,
+        # timestamp unit: the power of ten that makes the counter's window
+        # closest to the host's
+        dc = float(c1 - c0)
+        unit = min((1e-9, 1e-6, 1e-3, 1.0), key=lambda u: abs(np.log(max(dc * u, 1e-12) / sec)))
+        win = dc * unit
+        watts = j / win if win > 0 else None
+        tflops = flops * n / sec / 1e12
+        pmed = float(np.median(watts_s)) if watts_s else None
+        return {"warmup_seconds": round(warm, 2), "launches": n, "seconds": round(sec, 3),
+                "joules": round(j, 2), "counter_window_s": round(win, 3),
+                "avg_watts": round(watts, 1) if watts else None,
+                "TFLOP/s": round(tflops, 1),
+                "TFLOP/J": round(tflops / watts, 3) if watts else None,
+                "TFLOP/J_from_sampled_power": round(tflops / pmed, 3) if pmed else None,
+                "socket_watts_sampled_median": pmed,
                 "gfx_mhz_sampled_median": float(np.median(mhz)) if mhz else None,
-                "samples": len(watts)}
+                "gfx_mhz_sampled_p10": float(np.percentile(mhz, 10)) if mhz else None,
+                "samples": len(watts_s)}
     except Exception as e:
         return {"error": "energy read failed: %s" % e}
     finally:
@@ -493,6 +519,8 @@ def main():
                      "kernel_ms_p10_median_p90": [round(float(x), 4) for x in
                                                   np.percentile(kern_ms, [10, 50, 90])],
                      "sclk_mhz_profiled": prof["sclk_mhz"],
+                     "mfma_busy_profiled": prof["mfma_busy"],
+                     "valu_busy_profiled": prof["valu_busy"],
                      "frac_clock_adjusted": (round(achieved / (PEAK_TFLOPS[dtname] *
                                                                prof["sclk_mhz"] / 2400.0), 4)
                                              if prof["sclk_mhz"] else None),

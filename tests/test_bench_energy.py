@@ -2,6 +2,7 @@
 torch: joules from the accumulator difference, the PCI-bus device match, and
 the error records when amdsmi is missing or no device matches."""
 import sys
+import time
 import types
 
 import pytest
@@ -31,7 +32,7 @@ def fake_amdsmi(buses, uj_per_launch, resolution=15.3):
     m.amdsmi_get_gpu_device_bdf = lambda h: "0000:%02x:00.0" % buses[h]
     m.amdsmi_get_energy_count = lambda h: {
         "energy_accumulator": int(state["launches"] * uj_per_launch / resolution),
-        "counter_resolution": resolution, "timestamp": 0}
+        "counter_resolution": resolution, "timestamp": time.perf_counter_ns()}
     m.amdsmi_get_power_info = lambda h: {"current_socket_power": 1000, "power_limit": "N/A"}
     m.amdsmi_get_clock_info = lambda h, t: {"clk": 2100}
 
@@ -55,12 +56,15 @@ def test_energy_from_accumulator(with_amdsmi):
 
     def step():
         state["launches"] += 1
+        time.sleep(0.001)
     flops = 4e12
     r = bench.energy_run(step, flops, FakeTorch, seconds=0.0)
     n = r["launches"]
     assert n == 10                                  # the minimum loop
     assert r["joules"] == pytest.approx(2.0 * n, rel=1e-3)
-    assert r["TFLOP/J"] == pytest.approx(flops / 2.0 / 1e12, rel=1e-3)
+    # power from the counter's own timestamps (here host nanoseconds)
+    assert r["counter_window_s"] == pytest.approx(r["seconds"], rel=5e-2)
+    assert r["TFLOP/J"] == pytest.approx(flops / 2.0 / 1e12, rel=5e-2)
     assert r["socket_watts_sampled_median"] is None or r["socket_watts_sampled_median"] == 1000
     assert state["shut"]
 
