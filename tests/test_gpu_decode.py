@@ -116,3 +116,21 @@ def test_decode_stale_lengths_are_clamped(oracle):
     o, lse = pkg.flash_attn_decode_paged(dev[0], dev[1], dev[2], dev[3], bad, 64)
     torch.cuda.synchronize()
     _compare(oracle, synth.BF16, host, ds, [64, 0], o, lse, 1.0 / math.sqrt(128))
+
+
+def test_decode_out_of_range_pages_are_clamped(oracle):
+    """Block-table entries outside [0, pages) are clamped into the pool
+    (documented: results unspecified, accesses in bounds): the call returns,
+    the output is finite, and the rows whose pages are all valid are exact."""
+    lens = [40, 40]
+    host, ds, dev = _inputs(oracle, synth.BF16, lens, 2, 2, 128, 16, 12)
+    bad = dev[3].clone()
+    bad[1, 0] = -7                  # sequence 1: first page below the pool
+    bad[1, 2] = 1 << 20             # and its last page far past it
+    o, lse = pkg.flash_attn_decode_paged(dev[0], dev[1], dev[2], bad, dev[4], 40)
+    torch.cuda.synchronize()
+    go = o.float().cpu().numpy()
+    assert np.isfinite(go).all() and np.isfinite(lse.cpu().numpy()).all()
+    ro, rl = oracle.decode_paged(*host, np.asarray(lens), synth.BF16, 1.0 / math.sqrt(128))
+    err = np.linalg.norm(go[0] - ro[0]) / np.linalg.norm(ro[0])
+    assert err <= ROW_TOL, err

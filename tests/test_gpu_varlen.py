@@ -71,3 +71,23 @@ def test_equal_lengths_equal_dense_bitwise(oracle, dtype):
     # lse: varlen [H, B*L], dense [B, H, L]
     assert torch.equal(lv.view(H, B, L).permute(1, 0, 2).contiguous().view(torch.int32),
                        ld.view(torch.int32))
+
+
+def test_malformed_offsets_are_clamped(oracle):
+    """cu_seqlens entries outside [0, total] or decreasing are clamped by the
+    kernels (documented: results unspecified, accesses in bounds): the call
+    returns and the well-formed sequences are still exact."""
+    lens = [100, 50, 200]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total, H = int(cu[-1]), 2
+    enc, ds, dev = _packed(oracle, synth.BF16, total, H, 128, 404)
+    bad = cu.copy()
+    bad[2] = 10 ** 6       # sequence 1 ends past total, sequence 2 starts past it
+    o, lse = pkg.flash_attn_varlen_func(*dev, torch.from_numpy(bad).to(DEV), 200)
+    torch.cuda.synchronize()
+    go = o.float().cpu().numpy().astype(np.float64)
+    # sequence 0 is untouched by the bad entry
+    seq = [np.ascontiguousarray(x[0:100][None]) for x in enc]
+    ro, _ = oracle.attention(*seq, synth.BF16, 1.0 / np.sqrt(128), True)
+    pooled, rms, worst = errors(go[0:100][None], ro)
+    assert pooled <= TOL[synth.BF16] and worst <= TOL[synth.BF16], (pooled, worst)
