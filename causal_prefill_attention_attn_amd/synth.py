@@ -122,7 +122,7 @@ class DecodeWorkload:
     """One decode step: B sequences each add one query token and attend to
     their cached keys, held in pages of page_size slots.  The 32 query heads on
     8 key/value heads of D1-D3 are the head layout of Mistral-7B and Qwen3-8B,
-    two of the models the pages capture activations from; D4 has one
+    two of the models the pages capture activations from; D4 and D5 have one
     key/value head per query head."""
     name: str
     index: int
@@ -169,6 +169,8 @@ DECODE_WORKLOADS = {
                          "H_q=32 on H_kv=8, d=128, pages of 64"),
     "D4": DecodeWorkload("D4", 23, BF16, 16, 32, 32, 128, 128, 64, "uniform:16384",
                          "BF16 decode, B=16 L=16384, H_q=H_kv=32, d=128, pages of 64"),
+    "D5": DecodeWorkload("D5", 24, FP8, 16, 32, 32, 128, 128, 64, "uniform:16384",
+                         "FP8 e4m3 decode, B=16 L=16384, H_q=H_kv=32, d=128, pages of 64"),
 }
 
 
