@@ -115,3 +115,13 @@ def test_bad_arguments_raise():
     with pytest.raises(pkg.AttnError) as e:
         pkg.flash_attn_func(y, y, y, softmax_scale=float("nan"))
     assert e.value.status == -5
+
+
+def test_c2x_full_size_sampled_rows(oracle):
+    """The BF16 workload at 32K (B1 H32 S32768): sampled rows of three heads."""
+    w = synth.WORKLOADS["C2x"]
+    print("case C2x", flush=True)
+    enc, ds, dev = make_inputs(oracle, w)
+    o, lse = run_gpu(dev, w, ds)
+    rows = synth.sample_rows(w.S, 64)
+    check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, 13, 31])
