@@ -186,15 +186,18 @@ def _element_dtype(t) -> int:
 
 
 def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_descale=1.0,
-                    v_descale=1.0, out=None, lse=None, return_lse=True, hadamard_o=False):
+                    v_descale=1.0, out=None, lse=None, return_lse=True, hadamard_o=False,
+                    exact_p=False):
     """Forward attention on [B, S, H, D] tensors.
 
     q, k: [B, S, H, d_qk]; v: [B, S, H, d_v]; all bfloat16, or all FP8 e4m3
     (``torch.float8_e4m3fn`` or uint8 codes) with per-tensor descales.
     ``hadamard_o`` (FP8): rows of O are multiplied by the normalised Hadamard
     matrix, undoing a V rotated before quantization (``quantize_fp8(v,
-    rotate=True)``).  Returns ``(o, lse)``: o bfloat16 [B, S, H, d_v], lse
-    float32 [B, H, S] (natural log); lse is None when ``return_lse`` is False.
+    rotate=True)``).  ``exact_p`` (FP8): probabilities by exp2 and a rounding
+    conversion instead of the lean form.  Returns ``(o, lse)``: o bfloat16
+    [B, S, H, d_v], lse float32 [B, H, S] (natural log); lse is None when
+    ``return_lse`` is False.
     """
     torch = _torch()
     dt = _element_dtype(q)
@@ -219,7 +222,8 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_d
     st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                      lse.data_ptr() if lse is not None else None, B, S, H, d_qk, d_v,
                      float(softmax_scale), int(bool(causal)), dt, float(q_descale),
-                     float(k_descale), float(v_descale), 1 if hadamard_o else 0,
+                     float(k_descale), float(v_descale),
+                     (1 if hadamard_o else 0) | (2 if exact_p else 0),
                      _stream_handle(q.device))
     _check(st, "attn_fwd_ex")
     return out, lse

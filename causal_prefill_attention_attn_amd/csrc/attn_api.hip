@@ -63,8 +63,8 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, const 
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP8) return ATTN_ERR_DTYPE;
   if (!((d_qk == 128 || d_qk == 192) && d_v == 128) || (causal != 0 && causal != 1))
     return ATTN_ERR_UNSUPPORTED;
-  if ((flags & ~ATTN_FLAG_HADAMARD_O) != 0 ||
-      ((flags & ATTN_FLAG_HADAMARD_O) && dtype != ATTN_DTYPE_FP8))
+  if ((flags & ~(ATTN_FLAG_HADAMARD_O | ATTN_FLAG_EXACT_P)) != 0 ||
+      (flags != 0 && dtype != ATTN_DTYPE_FP8))
     return ATTN_ERR_UNSUPPORTED;
   if (!finite_positive(softmax_scale)) return ATTN_ERR_SCALE;
   if (dtype == ATTN_DTYPE_FP8 &&
@@ -95,7 +95,8 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, const 
   else
     rc = cpattn::launch_attn_fp8(q, k, v, o, lse, cu, total, (int)B, (int)S, (int)H, d_qk,
                                  softmax_scale, causal, q_descale, k_descale, v_descale,
-                                 (flags & ATTN_FLAG_HADAMARD_O) != 0, st);
+                                 (flags & ATTN_FLAG_HADAMARD_O) != 0,
+                                 (flags & ATTN_FLAG_EXACT_P) != 0, st);
   return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

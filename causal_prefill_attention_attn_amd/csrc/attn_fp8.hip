@@ -60,8 +60,6 @@
 // loads issued three tiles ahead (rows past the end read as zero).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include "attn_device.h"
 #include "attn_kernels.h"
@@ -456,24 +454,18 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
 int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
                     float softmax_scale, int causal, float q_descale, float k_descale,
-                    float v_descale, bool rot_o, hipStream_t stream) {
+                    float v_descale, bool rot_o, bool exact_p, hipStream_t stream) {
   const int occ = 2;                      // waves per SIMD (register budget)
   const int bm = 128 * occ;               // query rows per workgroup
   const int nqb = (S + bm - 1) / bm;
   const int BH = B * H;
   const dim3 grid((unsigned)nqb * (unsigned)BH);
   const float c_log2 = softmax_scale * q_descale * k_descale * 1.4426950408889634f;
-  // running-max refresh threshold (log2 units, 0..8); 0 = refresh on any increase
-  static const float lazy_log2 = [] {
-    const char* e = getenv("CPATTN_FP8_LAZY_LOG2");
-    float x = e ? strtof(e, nullptr) : 0.0f;
-    return (x >= 0.0f && x <= 8.0f) ? x : 0.0f;
-  }();
-  // probability form: "lean" (default) or "exact"
-  static const bool lean = [] {
-    const char* e = getenv("CPATTN_FP8_P");
-    return !(e && strcmp(e, "exact") == 0);
-  }();
+  // running-max refresh threshold (log2 units): 0 refreshes on any increase,
+  // which keeps the dominant probability of a peaked row exact; the kernel
+  // also supports up to 8 (fewer rescales, at some cost in accuracy)
+  const float lazy_log2 = 0.0f;
+  const bool lean = !exact_p;  // probabilities: lean (default) or exact exp2 + convert
 #define CPATTN_LAUNCH_FP8(DQK, BN, LEAN, OCC)                                                     \
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, BN, LEAN, OCC>), grid, dim3(256 * OCC), 0, stream, \
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, cu, \

@@ -16,11 +16,12 @@ int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float
                      float softmax_scale, int causal, hipStream_t stream);
 
 // FP8 E4M3FN q/k/v with per-tensor descales, d_qk in {128, 192}, d_v = 128;
-// rot_o: O rows times the normalised Hadamard matrix of order 128.
+// rot_o: O rows times the normalised Hadamard matrix of order 128; exact_p:
+// probabilities by exp2 and a rounding conversion instead of the lean form.
 int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
                     float softmax_scale, int causal, float q_descale, float k_descale,
-                    float v_descale, bool rot_o, hipStream_t stream);
+                    float v_descale, bool rot_o, bool exact_p, hipStream_t stream);
 
 int launch_amax_f32(const float* x, int64_t n, float* amax_out, hipStream_t stream);
 int launch_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out,

@@ -51,6 +51,7 @@ extern "C" {
 
 /* flags of attn_fwd_ex */
 #define ATTN_FLAG_HADAMARD_O 1u /* O rows times the normalised Hadamard matrix (FP8 only) */
+#define ATTN_FLAG_EXACT_P 2u    /* FP8 probabilities by exp2 + rounding conversion */
 
 /* element types of q, k, v */
 #define ATTN_DTYPE_BF16 0 /* bfloat16 */
@@ -113,8 +114,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
  *          the rotation that "Precisao, estabilidade e efeito na pratica" on
  *          the miraibroadcast.com page credits with about half of the FP8
  *          error, without a separate pass over O.  FP8 only.
+ *          ATTN_FLAG_EXACT_P: each probability is computed as exp2 and
+ *          rounded to e4m3 by the hardware conversion, instead of the default
+ *          "lean" form (one multiply-add and an integer conversion giving the
+ *          e4m3 bit pattern of 2^y directly, "Como o motor de atencao FP8 da
+ *          Zyphra funciona" on the miraibroadcast.com page).  FP8 only.
  * Every other argument, check and return code is that of attn_fwd; unknown
- * flag bits, or ATTN_FLAG_HADAMARD_O with BF16, return ATTN_ERR_UNSUPPORTED.
+ * flag bits, or any flag with BF16, return ATTN_ERR_UNSUPPORTED.
  * With flags = 0 the results equal those of attn_fwd bit for bit.
  */
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,

@@ -198,8 +198,10 @@ def test_fwd_ex_flags(lib):
                  v_descale=1.0, flags=0)
         a.update(kw)
         return pkg.attn_fwd_ex(*a.values())
-    assert call(flags=2) == -4                   # unknown flag bit
+    assert call(flags=4) == -4                   # unknown flag bit
     assert call(flags=1, dtype=0) == -4          # the O rotation is FP8 only
+    assert call(flags=2, dtype=0) == -4          # so is exact P
+    assert call(flags=3, dtype=0) == -4
     assert call(flags=1, q=None) == -1
     assert call(flags=1, B=0) == -2
     assert call(flags=1, o=Q + 64) == -7

@@ -91,3 +91,32 @@ def test_full_size_sampled_rows(oracle, name):
     check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, w.H // 2, w.H - 1])
     del dev, o, lse
     torch.cuda.empty_cache()
+
+
+def _run_exact(dev, w, ds):
+    o, lse = pkg.flash_attn_func(*dev, softmax_scale=w.softmax_scale, causal=True,
+                                 q_descale=ds[0], k_descale=ds[1], v_descale=ds[2], exact_p=True)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("d_qk", [128, 192])
+@pytest.mark.parametrize("S", [7, 129, 1000])
+def test_exact_p_ragged_lengths(oracle, S, d_qk):
+    """Probabilities by exp2 and the rounding conversion (ATTN_FLAG_EXACT_P)."""
+    w = _w("exactp%d_%d" % (S, d_qk), 1, 2, S, d_qk=d_qk, index=90 + S % 7 + d_qk)
+    print("case", w.name, flush=True)
+    enc, ds, dev = make_inputs(oracle, w)
+    o, lse = _run_exact(dev, w, ds)
+    check(oracle, w, enc, ds, o, lse)
+
+
+def test_exact_p_full_size_sampled_rows(oracle):
+    w = synth.WORKLOADS["C4g"]
+    print("case C4g exact P", flush=True)
+    enc, ds, dev = make_inputs(oracle, w)
+    o, lse = _run_exact(dev, w, ds)
+    rows = synth.sample_rows(w.S, 32)
+    check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, 31])
+    del dev, o, lse
+    torch.cuda.empty_cache()
