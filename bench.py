@@ -14,6 +14,8 @@ Workloads (seeded synthetic inputs, recipes in causal_prefill_attention_attn_amd
   C3  FP8 e4m3, B1 H32 S16384 d128, N(0,1)
   C2  BF16, B1 H32 S4096 d128, N(0,1)
   C2x BF16, B1 H32 S32768 d128, N(0,1)
+  C5b BF16 MLA, B1 H16 S32768 d_qk192 d_v128, N(0,1)
+  C4h4 FP8 e4m3, B1 H4 S32768 d128, LLM-like (one GPU's share of C4's heads)
 FLOPs per step: B*H*S^2*(d_qk+d_v) (both products over the causal half).
 """
 from __future__ import annotations

@@ -70,6 +70,9 @@ WORKLOADS = {
     # one GPU's share when C4's 32 heads are split over eight GPUs
     "C4h4": Workload("C4h4", 7, FP8, 1, 4, 32768, 128, 128, "llm",
                      "FP8 e4m3 causal fwd, B=1 H=4 S=32768 d=128, LLM-like (1/8 of C4's heads)"),
+    # the MLA shape in BF16
+    "C5b": Workload("C5b", 8, BF16, 1, 16, 32768, 192, 128, "gaussian",
+                    "BF16 causal MLA fwd, B=1 H=16 S=32768 d_qk=192 d_v=128, N(0,1)"),
 }
 
 

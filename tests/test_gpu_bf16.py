@@ -125,3 +125,13 @@ def test_c2x_full_size_sampled_rows(oracle):
     o, lse = run_gpu(dev, w, ds)
     rows = synth.sample_rows(w.S, 64)
     check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, 13, 31])
+
+
+def test_c5b_full_size_sampled_rows(oracle):
+    """BF16 in the MLA shape at 32K (B1 H16 S32768, d_qk 192, d_v 128)."""
+    w = synth.WORKLOADS["C5b"]
+    print("case C5b", flush=True)
+    enc, ds, dev = make_inputs(oracle, w)
+    o, lse = run_gpu(dev, w, ds)
+    rows = synth.sample_rows(w.S, 48)
+    check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, 15])
