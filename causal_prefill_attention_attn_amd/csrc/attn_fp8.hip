@@ -77,6 +77,13 @@ __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int scale_
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
 }
 
+// Keep a value's computation above this point: the empty volatile statement
+// reads and rewrites the registers, so the instructions that produce them
+// cannot sink below a later barrier (they touch no memory, so the compiler
+// would otherwise move them into the next iteration).
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 // 16-byte chunk swizzle of a V row (128 bytes = 8 chunks) so that the eight
 // key rows one ds_read_b64_tr_b8 touches fall in distinct LDS banks
 __device__ __forceinline__ int v_swz(int key) { return ((key >> 1) & 1) * 2 + ((key >> 3) & 1) * 4; }
@@ -167,13 +174,17 @@ struct Smem {
 // One workgroup of 4*kOcc waves per compute unit (kOcc waves per SIMD),
 // each wave owning 32 query rows; the 32*4*kOcc rows of the workgroup share
 // every K/V tile in LDS, which keeps K/V re-reads from L2 low.  Each wave is
-// software-pipelined one tile deep: in iteration t it issues the matrix
-// instructions of S(t+1) = K(t+1).Q^T and then computes the probabilities of
-// tile t on the vector unit while those run, so its own matrix and vector
-// work overlap; the other wave of the SIMD fills the remaining gaps (the
-// overlap of matrix and vector work that "Como o motor de atencao FP8 da
-// Zyphra funciona" on the miraibroadcast.com page describes, obtained here
-// from instruction order inside each wave).  One workgroup barrier per tile.
+// software-pipelined one tile deep and carries the scores of the next tile
+// and their row maximum from one iteration to the next.  Iteration t forms
+// P(t) on the vector unit while the matrix unit computes S(t+1) = K(t+1).Q^T,
+// then runs O += P(t).V(t) on the matrix unit while the vector unit takes the
+// row maximum of S(t+1).  Both halves are branch-free in the iterations whose
+// next tile needs no mask, so the compiler spreads the matrix instructions
+// through the vector work of the same wave, and the other wave of the SIMD
+// fills the remaining gaps (the overlap of matrix and vector work that "Como
+// o motor de atencao FP8 da Zyphra funciona" on the miraibroadcast.com page
+// describes, obtained here from instruction order inside each wave).  One
+// workgroup barrier per tile.
 template <int DQK, int BN, bool kLean, int kOcc>
 __global__ void __launch_bounds__(256 * kOcc, 1)
 attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
@@ -195,7 +206,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int col = lane & 31;
   const int half = lane >> 5;
 
@@ -302,6 +313,11 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       }
   };
   auto active = [&](int t) { return t < nkt && !(causal && t * BN > q0w + 31); };
+  // tile t needs the mask (diagonal or ragged) for some row of this wave
+  auto masked = [&](int t) {
+    const int key0 = t * BN;
+    return (causal && key0 + BN - 1 > q0w) || key0 + BN > S;
+  };
 
   f32x16 oacc[kDV / 32];
 #pragma unroll
@@ -310,121 +326,187 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   float m_run = -INFINITY;  // max of c*s in use (log2 domain)
   f32x16 sa[2], sb[2];      // score buffers of consecutive tiles
 
-  // ---- prologue: tiles 0..2 issued, 0 and 1 complete, S(0) started
+  // mask of tile t (diagonal or ragged) applied to its scores
+  auto apply_mask = [&](int t, f32x16* s) {
+    const int key0 = t * BN;
+    const int lim = (causal ? min(q0w + col, S - 1) : S - 1) - key0;  // last visible offset
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kofs = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+        s[kb][i] = kofs > lim ? -INFINITY : s[kb][i];
+      }
+  };
+  // largest c*s of the row in a tile (block 0 chain, then block 1)
+  auto tile_max = [&](const f32x16* s) {
+    float mx0 = fmaxf(s[0][0], s[0][1]), mx1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) mx0 = fmaxf(fmaxf(mx0, s[0][i]), s[0][i + 1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) mx1 = fmaxf(fmaxf(mx1, s[1][i]), s[1][i + 1]);
+    return pair_max(fmaxf(mx0, mx1)) * c_log2;
+  };
+  // running max refresh; O and l rescaled when some row's max grows
+  auto refresh = [&](float bmax) {
+    if (__any(bmax > m_run + lazy_log2)) {
+      const float m_new = fmaxf(m_run, bmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < kDV / 32; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      lacc[0] *= alpha;
+    }
+  };
+  // P = e4m3(2^(c*s - m + k)); k = 8 - ceil(block max - m) puts the block
+  // maximum in (2^7, 2^8]; k >= 0 since block max - m <= lazy_log2 <= 8
+  auto probs = [&](const f32x16* scur, float bmax, int& pscale) {
+    const float kf = fminf(8.0f - __builtin_ceilf(bmax - m_run), 126.0f);
+    pscale = kE8M0One - (int)kf;
+    i32x8 pw = __builtin_nondeterministic_value(pw);  // every byte is written below
+    if constexpr (kLean) {
+      const float c8 = 8.0f * c_log2;
+      const float ofs8 = 8.0f * (7.0f + kf - m_run) - kLeanShift;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2;
+        const int i0 = (w & 3) * 4;
+        unsigned word = (unsigned)pw[w];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(scur[kb][i0 + e], c8, ofs8), e, word);
+        pw[w] = (int)word;
+      }
+    } else {
+      const float ofs = kf - m_run;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2;
+        const int i0 = (w & 3) * 4;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 0], c_log2, ofs));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 1], c_log2, ofs));
+        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 2], c_log2, ofs));
+        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 3], c_log2, ofs));
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+        pw[w] = word;
+      }
+    }
+    return pw;
+  };
+  // O^T += V^T . P^T and l += ones . P^T; V^T operands of the four 32-row
+  // blocks of d read two blocks ahead (inline assembly: the reads wait for
+  // no buffer-to-LDS load in flight)
+  auto pv = [&](int t, const i32x8& pw, int pscale) {
+    const uint32_t vt = lds_addr(sm.v[t % LY::kStages]);
+    i32x2 r[2][4];
+    auto vread = [&](int d, i32x2* x) {
+      const uint32_t a = vt + (vbase ^ (d << 5));
+      x[0] = ds_read_tr8<0 * 16 * kDV>(a);
+      x[1] = ds_read_tr8<1 * 16 * kDV>(a);
+      x[2] = ds_read_tr8<2 * 16 * kDV>(a);
+      x[3] = ds_read_tr8<3 * 16 * kDV>(a);
+    };
+    vread(0, r[0]);
+    vread(1, r[1]);
+#pragma unroll
+    for (int d = 0; d < kDV / 32; ++d) {
+      i32x2* x = r[d & 1];
+      if (d + 1 < kDV / 32) lds_wait4<4>(x[0], x[1], x[2], x[3]);  // block d+1 may be in flight
+      else lds_wait4<0>(x[0], x[1], x[2], x[3]);
+      const i32x8 a = __builtin_shufflevector(
+          __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3),
+          __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
+      if (d + 2 < kDV / 32) vread(d + 2, x);
+    }
+    lacc = mfma_f8(ones, pw, lacc, kE8M0One, pscale);
+  };
+
+  // ---- prologue: tiles 0..2 issued, 0 and 1 complete, S(0) and its max
+  float bmax_a = 0.0f, bmax_b = 0.0f;  // tile maxima of the two score buffers
 #pragma unroll
   for (int t = 0; t < 3; ++t)
     if (t < nkt) issue_tile(t);
   if (nkt > 2) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
   barrier_nofence();
-  if (active(0)) qk(0, sa);
+  if (active(0)) {
+    qk(0, sa);
+    if (masked(0)) apply_mask(0, sa);
+    bmax_a = tile_max(sa);
+  }
 
-  auto step = [&](int t, f32x16* scur, f32x16* snext) {
+  // Iteration t: P(t) from S(t) and its max, S(t+1) = K(t+1).Q^T, O += P(t).V(t),
+  // then the max of S(t+1).  While tile t+1 is fully visible to every row of
+  // the wave (all but the last iterations of a wave) the iteration is two
+  // straight-line regions whose matrix instructions are interleaved with the
+  // vector work: P(t) alongside S(t+1), and the max of S(t+1) alongside
+  // O += P(t).V(t).  The remaining iterations (masked or inactive tiles) run
+  // the general form.  Every iteration ends in one workgroup barrier, so all
+  // waves pass the same number of barriers.
+  auto fast_step = [&](int t, f32x16* scur, f32x16* snext, float bcur, float& bnext) {
     // tile t+3 goes to the buffer of tile t-1, finished before the last barrier
     const bool more = t + 3 < nkt;
     if (more) issue_tile(t + 3);
-    // S(t+1) on the matrix unit while the probabilities of tile t are computed
-    if (active(t + 1)) qk(t + 1, snext);
-    if (active(t)) {
-      const int key0 = t * BN;
-      if ((causal && key0 + BN - 1 > q0w) || key0 + BN > S) {
-        const int lim = (causal ? min(q0w + col, S - 1) : S - 1) - key0;  // last visible offset
+    refresh(bcur);
+    int pscale;
+    const i32x8 pw = probs(scur, bcur, pscale);
+    qk(t + 1, snext);
+    pv(t, pw, pscale);
+    bnext = tile_max(snext);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kofs = kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            scur[kb][i] = kofs > lim ? -INFINITY : scur[kb][i];
-          }
-      }
-      // two chains of three-input maxima (16 v_max3 for 32 scores)
-      float mx0 = fmaxf(scur[0][0], scur[1][0]), mx1 = fmaxf(scur[0][1], scur[1][1]);
-#pragma unroll
-      for (int i = 2; i < 16; i += 2) {
-        mx0 = fmaxf(fmaxf(mx0, scur[0][i]), scur[1][i]);
-        mx1 = fmaxf(fmaxf(mx1, scur[0][i + 1]), scur[1][i + 1]);
-      }
-      const float mx = fmaxf(mx0, mx1);
-      const float bmax = pair_max(mx) * c_log2;
-      if (__any(bmax > m_run + lazy_log2)) {
-        const float m_new = fmaxf(m_run, bmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-#pragma unroll
-        for (int d = 0; d < kDV / 32; ++d)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-        lacc[0] *= alpha;
-      }
-      // P = e4m3(2^(c*s - m + k)); k = 8 - ceil(block max - m) puts the block
-      // maximum in (2^7, 2^8]; k >= 0 since block max - m <= lazy_log2 <= 8
-      const float kf = fminf(8.0f - __builtin_ceilf(bmax - m_run), 126.0f);
-      const int pscale = kE8M0One - (int)kf;
-      i32x8 pw = __builtin_nondeterministic_value(pw);  // every byte is written below
-      if constexpr (kLean) {
-        const float c8 = 8.0f * c_log2;
-        const float ofs8 = 8.0f * (7.0f + kf - m_run) - kLeanShift;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int kb = w >> 2;
-          const int i0 = (w & 3) * 4;
-          unsigned word = (unsigned)pw[w];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(scur[kb][i0 + e], c8, ofs8), e, word);
-          pw[w] = (int)word;
-        }
-      } else {
-        const float ofs = kf - m_run;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int kb = w >> 2;
-          const int i0 = (w & 3) * 4;
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 0], c_log2, ofs));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 1], c_log2, ofs));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 2], c_log2, ofs));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i0 + 3], c_log2, ofs));
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-          pw[w] = word;
-        }
-      }
-      // ---- O^T += V^T . P^T and l += ones . P^T
-      // V^T operands of the four 32-row blocks of d, read two blocks ahead
-      // (inline assembly: the reads wait for no buffer-to-LDS load in flight)
-      const uint32_t vt = lds_addr(sm.v[t % LY::kStages]);
-      i32x2 r[2][4];
-      auto vread = [&](int d, i32x2* x) {
-        const uint32_t a = vt + (vbase ^ (d << 5));
-        x[0] = ds_read_tr8<0 * 16 * kDV>(a);
-        x[1] = ds_read_tr8<1 * 16 * kDV>(a);
-        x[2] = ds_read_tr8<2 * 16 * kDV>(a);
-        x[3] = ds_read_tr8<3 * 16 * kDV>(a);
-      };
-      vread(0, r[0]);
-      vread(1, r[1]);
-#pragma unroll
-      for (int d = 0; d < kDV / 32; ++d) {
-        i32x2* x = r[d & 1];
-        if (d + 1 < kDV / 32) lds_wait4<4>(x[0], x[1], x[2], x[3]);  // block d+1 may be in flight
-        else lds_wait4<0>(x[0], x[1], x[2], x[3]);
-        const i32x8 a = __builtin_shufflevector(
-            __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3),
-            __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
-        if (d + 2 < kDV / 32) vread(d + 2, x);
-      }
-      lacc = mfma_f8(ones, pw, lacc, kE8M0One, pscale);
-    }
+    for (int d = 0; d < kDV / 32; ++d) pin(oacc[d]);
+    pin(lacc);
+    pin(bnext);
     // tile t+2 must be complete for S(t+2) in the next iteration: each wave
     // waits for its own loads of it, then the barrier (no fence: a release
     // would wait for the loads of tile t+3 as well)
     if (more) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
     barrier_nofence();
   };
-  // unrolled by two so that the two score buffers swap roles without copies
-  for (int t = 0; t < nkt; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < nkt) step(t + 1, sb, sa);
+  auto slow_step = [&](int t, f32x16* scur, f32x16* snext, float bcur, float& bnext) {
+    const bool more = t + 3 < nkt;
+    if (more) issue_tile(t + 3);
+    if (active(t)) {
+      refresh(bcur);
+      int pscale;
+      const i32x8 pw = probs(scur, bcur, pscale);
+      if (active(t + 1)) qk(t + 1, snext);
+      pv(t, pw, pscale);
+      if (active(t + 1)) {
+        if (masked(t + 1)) apply_mask(t + 1, snext);
+        bnext = tile_max(snext);
+      }
+    }
+    if (more) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
+    barrier_nofence();
+  };
+  // first iteration whose next tile is masked: iterations below it take the
+  // straight-line form (tile t+1 < nkt is then fully visible)
+  int t_fe = 0;
+  {
+    const int lim = causal ? min(q0w + 1, S) : S;   // keys [0, lim) visible to every row
+    t_fe = max(0, lim / BN - 1);
+  }
+  // unrolled by two so that the two score buffers swap roles without copies;
+  // an odd exit copies the scores once
+  int t = 0;
+  for (; t + 1 < t_fe; t += 2) {
+    fast_step(t, sa, sb, bmax_a, bmax_b);
+    fast_step(t + 1, sb, sa, bmax_b, bmax_a);
+  }
+  if (t < t_fe) {
+    fast_step(t, sa, sb, bmax_a, bmax_b);
+    sa[0] = sb[0];
+    sa[1] = sb[1];
+    bmax_a = bmax_b;
+    ++t;
+  }
+  for (; t < nkt; t += 2) {
+    slow_step(t, sa, sb, bmax_a, bmax_b);
+    if (t + 1 < nkt) slow_step(t + 1, sb, sa, bmax_b, bmax_a);
   }
 
   // ---- epilogue
