@@ -46,6 +46,13 @@ namespace cpattn {
 
 namespace {
 
+// Keep a value's computation above this point: the empty volatile statement
+// reads and rewrites the registers, so the instructions that produce them
+// cannot sink below a later barrier (they touch no memory, so the compiler
+// would otherwise move them into the next iteration).
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 constexpr int kWaves = 8;            // waves per workgroup, two per SIMD
 constexpr int kBM = 32 * kWaves;     // query rows per workgroup
 constexpr int kDV = 128;             // value head dimension
@@ -198,6 +205,11 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int vbase = vrow * kVRow + (gj & 3) * 8 + ((vgrp ^ v_swz(vrow)) << 5);
 
   auto active = [&](int t) { return t < nkt && !(causal && t * BN > q0w + 31); };
+  // tile t needs the mask (diagonal or ragged) for some row of this wave
+  auto masked = [&](int t) {
+    const int key0 = t * BN;
+    return (causal && key0 + BN - 1 > q0w) || key0 + BN > S;
+  };
 
   f32x16 oacc[kDV / 32];
 #pragma unroll
@@ -216,115 +228,170 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kt, kb, s), qreg[s], sc[kb], 0, 0, 0);
     }
   };
+  // mask of tile t (diagonal and ragged-tail tiles only)
+  auto apply_mask = [&](int t, f32x16* sc) {
+    // last visible key offset, less this lane half's 4-key shift, so the
+    // comparisons below are against compile-time constants
+    const int lim = (causal ? min(q0w + col, S - 1) : S - 1) - t * BN - half * 4;
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kofs = kb * 32 + (i >> 2) * 8 + (i & 3);
+        sc[kb][i] = kofs > lim ? -INFINITY : sc[kb][i];
+      }
+  };
+  // row max of a tile: two chains of three-input maxima (max(max(m, a), b)
+  // is one v_max3; max(m, max(a, b)) was compiled as two instructions)
+  auto tile_max = [&](const f32x16* sc) {
+    float ma = -INFINITY, mb = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        ma = fmaxf(fmaxf(ma, sc[kb][i]), sc[kb][i + 1]);
+        mb = fmaxf(fmaxf(mb, sc[kb][i + 2]), sc[kb][i + 3]);
+      }
+    return pair_max(fmaxf(ma, mb)) * c_log2;
+  };
+  auto refresh = [&](float tmax) {
+    if (__any(tmax > m_run)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < kDV / 32; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+    }
+  };
+  // P = exp2(c*s - m), bf16, laid out as the B operand of P.V; the row sum
+  // adds the rounded probabilities, two per v_dot2 against (1, 1)
+  auto probs = [&](const f32x16* scur, bf16x8* pb) {
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pb[kb * 2 + (i >> 3)][i & 7] =
+            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i], c_log2, -m_run));
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float psa = 0.f, psb = 0.f;
+#pragma unroll
+    for (int u = 0; u < BN / 16; ++u) {
+      psa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 0, 1), one2, psa, false);
+      psb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 2, 3), one2, psb, false);
+      psa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 4, 5), one2, psa, false);
+      psb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 6, 7), one2, psb, false);
+    }
+    l_run += psa + psb;
+  };
+  // O^T += V^T . P^T, V^T reads two operands ahead of their use
+  auto pv = [&](int t, const bf16x8* pb) {
+    constexpr int kPV = (BN / 16) * (kDV / 32);
+    const uint32_t vt = lds_addr(sm.v[t % kStages]);
+    auto vread = [&](int m) {
+      const int u = m / (kDV / 32), d = m % (kDV / 32);
+      const uint32_t a = vt + u * 16 * kVRow + (vbase ^ (d << 6));
+      const i16x4 ra = ds_read_tr16<0>(a);
+      const i16x4 rb = ds_read_tr16<8 * kVRow>(a);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vop[kPV];
+    vop[0] = vread(0);
+    vop[1] = vread(1);
+#pragma unroll
+    for (int m = 0; m < kPV; ++m) {
+      if (m + 2 < kPV) {
+        vop[m + 2] = vread(m + 2);
+        lds_wait_n<4>(vop[m]);
+      } else if (m + 1 < kPV) {
+        lds_wait_n<2>(vop[m]);
+      } else {
+        lds_wait_n<0>(vop[m]);
+      }
+      const int u = m / (kDV / 32), d = m % (kDV / 32);
+      oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m], pb[u], oacc[d], 0, 0, 0);
+    }
+  };
 
-  // ---- prologue: tiles 0..2 issued, 0 and 1 complete, S(0) started
+  // ---- prologue: tiles 0..2 issued, 0 and 1 complete, S(0) and its max
+  float tmax_a = 0.f, tmax_b = 0.f;  // row maxima of the two score buffers
 #pragma unroll
   for (int t = 0; t < kAhead; ++t)
     if (t < nkt) issue_tile(t);
   if (nkt > 2) wait_vmcnt<kMine>();
   else wait_vmcnt<0>();
   barrier_nofence();
-  if (active(0)) qk(0, sa);
+  if (active(0)) {
+    qk(0, sa);
+    if (masked(0)) apply_mask(0, sa);
+    tmax_a = tile_max(sa);
+  }
 
-  auto step = [&](int t, f32x16* scur, f32x16* snext) {
+  // Iteration t: P(t) from S(t) and its max, S(t+1) = K(t+1).Q^T, O += P(t).V(t),
+  // then the max of S(t+1).  While tile t+1 is fully visible to every row of
+  // the wave the iteration is branch-free apart from the rescale, so the
+  // compiler spreads the matrix instructions through the vector work of the
+  // same wave: P(t) alongside S(t+1), the max of S(t+1) alongside
+  // O += P(t).V(t).  Masked or inactive tiles take the general form.  Each
+  // iteration ends in one workgroup barrier.
+  static_assert(kAhead == 3, "wait counts assume three tiles ahead");
+  auto fast_step = [&](int t, f32x16* scur, f32x16* snext, float tcur, float& tnext) {
     // tile t+3 goes to the stage of tile t-1, finished before the last barrier
     if (t + kAhead < nkt) issue_tile(t + kAhead);
-    // S(t+1) on the matrix unit while the probabilities of tile t are formed
-    if (active(t + 1)) qk(t + 1, snext);
-    if (active(t)) {
-      const int key0 = t * BN;
-      // ---- mask (diagonal and ragged-tail tiles only), running max
-      if ((causal && key0 + BN - 1 > q0w) || key0 + BN > S) {
-        // last visible key offset, less this lane half's 4-key shift, so the
-        // comparisons below are against compile-time constants
-        const int lim = (causal ? min(q0w + col, S - 1) : S - 1) - key0 - half * 4;
+    refresh(tcur);
+    bf16x8 pb[BN / 16];
+    probs(scur, pb);
+    qk(t + 1, snext);
+    pv(t, pb);
+    tnext = tile_max(snext);
 #pragma unroll
-        for (int kb = 0; kb < kNKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kofs = kb * 32 + (i >> 2) * 8 + (i & 3);
-            scur[kb][i] = kofs > lim ? -INFINITY : scur[kb][i];
-          }
-      }
-      // row max: two chains of three-input maxima (max(max(m, a), b) is one
-      // v_max3; max(m, max(a, b)) was compiled as two instructions)
-      float ma = -INFINITY, mb = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kNKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-          ma = fmaxf(fmaxf(ma, scur[kb][i]), scur[kb][i + 1]);
-          mb = fmaxf(fmaxf(mb, scur[kb][i + 2]), scur[kb][i + 3]);
-        }
-      const float tmax = pair_max(fmaxf(ma, mb)) * c_log2;
-      if (__any(tmax > m_run)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < kDV / 32; ++d)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-      }
-      // ---- P = exp2(c*s - m), bf16, laid out as the B operand of P.V; the
-      // row sum adds the rounded probabilities, two per v_dot2 against (1, 1)
-      bf16x8 pb[BN / 16];
-#pragma unroll
-      for (int kb = 0; kb < kNKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          pb[kb * 2 + (i >> 3)][i & 7] =
-              (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i], c_log2, -m_run));
-      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-      float psa = 0.f, psb = 0.f;
-#pragma unroll
-      for (int u = 0; u < BN / 16; ++u) {
-        psa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 0, 1), one2, psa, false);
-        psb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 2, 3), one2, psb, false);
-        psa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 4, 5), one2, psa, false);
-        psb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 6, 7), one2, psb, false);
-      }
-      l_run += psa + psb;
-
-      // ---- O^T += V^T . P^T, V^T reads two operands ahead of their use
-      constexpr int kPV = (BN / 16) * (kDV / 32);
-      const uint32_t vt = lds_addr(sm.v[t % kStages]);
-      auto vread = [&](int m) {
-        const int u = m / (kDV / 32), d = m % (kDV / 32);
-        const uint32_t a = vt + u * 16 * kVRow + (vbase ^ (d << 6));
-        const i16x4 ra = ds_read_tr16<0>(a);
-        const i16x4 rb = ds_read_tr16<8 * kVRow>(a);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8 vop[kPV];
-      vop[0] = vread(0);
-      vop[1] = vread(1);
-#pragma unroll
-      for (int m = 0; m < kPV; ++m) {
-        if (m + 2 < kPV) {
-          vop[m + 2] = vread(m + 2);
-          lds_wait_n<4>(vop[m]);
-        } else if (m + 1 < kPV) {
-          lds_wait_n<2>(vop[m]);
-        } else {
-          lds_wait_n<0>(vop[m]);
-        }
-        const int u = m / (kDV / 32), d = m % (kDV / 32);
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m], pb[u], oacc[d], 0, 0, 0);
-      }
-    }
-    // tile t+2 complete for S(t+2) in the next step (tile t+3 may stay in
-    // flight)
-    static_assert(kAhead == 3, "wait counts assume three tiles ahead");
+    for (int d = 0; d < kDV / 32; ++d) pin(oacc[d]);
+    pin(l_run);
+    pin(tnext);
+    // tile t+2 complete for S(t+2) in the next step (tile t+3 may stay in flight)
     if (t + 3 < nkt) wait_vmcnt<kMine>();
     else wait_vmcnt<0>();
     barrier_nofence();
   };
-  // unrolled by two so that the score buffers swap roles without copies
-  for (int t = 0; t < nkt; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < nkt) step(t + 1, sb, sa);
+  auto slow_step = [&](int t, f32x16* scur, f32x16* snext, float tcur, float& tnext) {
+    if (t + kAhead < nkt) issue_tile(t + kAhead);
+    if (active(t)) {
+      refresh(tcur);
+      bf16x8 pb[BN / 16];
+      probs(scur, pb);
+      if (active(t + 1)) qk(t + 1, snext);
+      pv(t, pb);
+      if (active(t + 1)) {
+        if (masked(t + 1)) apply_mask(t + 1, snext);
+        tnext = tile_max(snext);
+      }
+    }
+    if (t + 3 < nkt) wait_vmcnt<kMine>();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+  };
+  // iterations below t_fe have a fully visible next tile (t + 1 < nkt)
+  const int lim_all = causal ? min(q0w + 1, S) : S;  // keys [0, lim_all) visible to every row
+  const int t_fe = max(0, lim_all / BN - 1);
+  // unrolled by two so that the score buffers swap roles without copies; an
+  // odd exit copies the scores once
+  int t = 0;
+  for (; t + 1 < t_fe; t += 2) {
+    fast_step(t, sa, sb, tmax_a, tmax_b);
+    fast_step(t + 1, sb, sa, tmax_b, tmax_a);
+  }
+  if (t < t_fe) {
+    fast_step(t, sa, sb, tmax_a, tmax_b);
+#pragma unroll
+    for (int kb = 0; kb < kNKB; ++kb) sa[kb] = sb[kb];
+    tmax_a = tmax_b;
+    ++t;
+  }
+  for (; t < nkt; t += 2) {
+    slow_step(t, sa, sb, tmax_a, tmax_b);
+    if (t + 1 < nkt) slow_step(t + 1, sb, sa, tmax_b, tmax_a);
   }
 
   // ---- epilogue: O / l -> bf16, lse = ln2 * (m + log2 l)
