@@ -76,6 +76,12 @@ __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int scale_
   // operand formats 0/0 = E4M3 x E4M3; op_sel 0 = byte 0 of each scale VGPR
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
 }
+// The same product without block scales: zero scale operands select the
+// unscaled instruction (v_mfma_f32_32x32x64_f8f6f4), whose result equals the
+// scaled one with both scales 2^0 and which needs no scale registers.
+__device__ __forceinline__ f32x16 mfma_f8_plain(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
 
 // Keep a value's computation above this point: the empty volatile statement
 // reads and rewrites the registers, so the instructions that produce them
@@ -308,8 +314,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
         const uint8_t* kblk = kt + kb * 32 * LY::kKPitch;
         const i32x4 lo = *reinterpret_cast<const i32x4*>(kblk + (kbase ^ ((s * 4) << 4)));
         const i32x4 hi = *reinterpret_cast<const i32x4*>(kblk + (kbase ^ ((s * 4 + 1) << 4)));
-        sa[kb] = mfma_f8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qreg[s], sa[kb],
-                         kE8M0One, kE8M0One);
+        sa[kb] = mfma_f8_plain(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qreg[s], sa[kb]);
       }
   };
   auto active = [&](int t) { return t < nkt && !(causal && t * BN > q0w + 31); };
