@@ -60,6 +60,12 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kVRow = kDV * 2;       // bytes per V row
 constexpr int kAhead = 3;            // tiles loaded ahead of the current one
 constexpr int kStages = 4;
+// The running maximum m is refreshed (and O, l rescaled) only when a row's
+// tile maximum exceeds it by more than this many octaves, so probabilities
+// can reach 2^kLazyLog2.  P is rounded to bf16, a floating-point format, so
+// its relative rounding error does not depend on how far m lags the true
+// maximum; O, l and lse = m + log2(l) are the same up to that rounding.
+constexpr float kLazyLog2 = 8.0f;
 
 // 32-byte chunk swizzle of a V row: the four consecutive keys one transposed
 // read covers land on four distinct even chunk slots
@@ -255,7 +261,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     return pair_max(fmaxf(ma, mb)) * c_log2;
   };
   auto refresh = [&](float tmax) {
-    if (__any(tmax > m_run)) {
+    if (__any(tmax > m_run + kLazyLog2)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
