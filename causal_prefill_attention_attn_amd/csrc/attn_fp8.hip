@@ -23,10 +23,12 @@
 //                   32x32x64 instruction a lane's scale covers the 32-key
 //                   block held by bytes 0-15 (or 16-31) of both lane halves,
 //                   so both halves carry the same 64-key exponent.
-//   l               the row sum is taken from the rounded, de-scaled P that
-//                   enters P.V, with one extra matrix instruction per 64-key
-//                   block that multiplies P^T by a block of ones (same
-//                   section of that page).
+//   l               the row sum is taken from the rounded P that enters
+//                   P.V, with one extra matrix instruction per 64-key block
+//                   that multiplies P^T by a selector matrix of ones and
+//                   zeros (same section of that page): the half-size
+//                   16x16x128 instruction sums each lane's own query, and the
+//                   block's 2^-k is applied to that sum on the vector unit.
 //   O^T += V^T.P^T  A = V^T read from a row-major V tile in LDS with
 //                   ds_read_b64_tr_b8 (16 lanes cooperatively read 8 rows of
 //                   16 bytes and each receives one column), B = P^T straight
@@ -67,6 +69,8 @@
 namespace cpattn {
 
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDV = 128;
 constexpr int kE8M0One = 127;      // E8M0 encoding of 2^0
@@ -300,8 +304,20 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   // kbase ^ ((s*4 + part) << 4) with kbase = row offset | ((half*2 ^ swz) << 4)
   const int kbase = col * LY::kKPitch + (((half * 2) ^ LY::k_swz(col)) << 4);
 
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  // row sums on v_mfma_f32_16x16x128_f8f6f4: column n of its B operand is
+  // lanes n, n+16, n+32, n+48 of the P^T registers, i.e. queries n and n+16,
+  // each with both of its key halves.  Row m of the A operand comes from
+  // lanes m, m+16, m+32, m+48; rows 0 and 8 select the lane groups of query
+  // n, rows 4 and 12 those of query n+16, so output row 4*(l/16) of lane l
+  // (its first accumulator register) is the sum over the tile of lane l's
+  // own query.
+  i32x8 lsel;
+  {
+    const int m = lane & 15, g = lane >> 4;
+    const bool on = ((m == 0 || m == 8) && !(g & 1)) || ((m == 4 || m == 12) && (g & 1));
+    const int v = on ? 0x38383838 : 0;  // e4m3 1.0 or 0
+    lsel = i32x8{v, v, v, v, v, v, v, v};
+  }
 
   auto qk = [&](int t, f32x16* sa) {  // S^T of tile t = K(t) . Q^T, two 32-key blocks
     const uint8_t* kt = sm.k[t % LY::kStages];
@@ -327,7 +343,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   f32x16 oacc[kDV / 32];
 #pragma unroll
   for (int i = 0; i < kDV / 32; ++i) oacc[i] = f32x16{};
-  f32x16 lacc = f32x16{};   // every entry of a column holds the same row sum
+  float l_run = 0.f;        // row sum of this lane's query
   float m_run = -INFINITY;  // max of c*s in use (log2 domain)
   f32x16 sa[2], sb[2];      // score buffers of consecutive tiles
 
@@ -362,7 +378,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       for (int d = 0; d < kDV / 32; ++d)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
-      lacc[0] *= alpha;
+      l_run *= alpha;
     }
   };
   // P = e4m3(2^(c*s - m + k)); k = 8 - ceil(block max - m) puts the block
@@ -401,7 +417,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     }
     return pw;
   };
-  // O^T += V^T . P^T and l += ones . P^T; V^T operands of the four 32-row
+  // O^T += V^T . P^T and the row sum of P; V^T operands of the four 32-row
   // blocks of d read two blocks ahead (inline assembly: the reads wait for
   // no buffer-to-LDS load in flight)
   auto pv = [&](int t, const i32x8& pw, int pscale) {
@@ -427,7 +443,10 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
       if (d + 2 < kDV / 32) vread(d + 2, x);
     }
-    lacc = mfma_f8(ones, pw, lacc, kE8M0One, pscale);
+    {
+      const f32x4 lt = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lsel, pw, f32x4{}, 0, 0, 0, 0, 0, 0);
+      l_run = __builtin_fmaf(lt[0], __uint_as_float((unsigned)pscale << 23), l_run);
+    }
   };
 
   // ---- prologue: tiles 0..2 issued, 0 and 1 complete, S(0) and its max
@@ -463,7 +482,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     bnext = tile_max(snext);
 #pragma unroll
     for (int d = 0; d < kDV / 32; ++d) pin(oacc[d]);
-    pin(lacc);
+    pin(l_run);
     pin(bnext);
     // tile t+2 must be complete for S(t+2) in the next iteration: each wave
     // waits for its own loads of it, then the barrier (no fence: a release
@@ -516,7 +535,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
 
   // ---- epilogue
   if (rot_o) hadamard_o_rows(oacc, half);
-  const float l_tot = lacc[0];
+  const float l_tot = l_run;
   const int qi = q0w + col;
   if (qi < S) {
     // 1/sqrt(128) normalises the rotation
