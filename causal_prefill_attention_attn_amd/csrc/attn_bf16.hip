@@ -25,8 +25,8 @@
 // so that the eight 32-byte pieces one read instruction touches per 32
 // lanes fall in distinct banks; K rows with a 16-byte chunk swizzle so that
 // 16 consecutive keys read 16 distinct chunks.  The row sum adds the
-// bf16-rounded probabilities that enter P.V (v_dot2 of pairs against
-// (1, 1), fp32 accumulation).
+// bf16-rounded probabilities that enter P.V on the matrix unit (16x16x32
+// products of each P^T block with a lane-group selector, fp32 accumulation).
 //
 // Schedule: eight waves per workgroup (two per SIMD) share every K/V tile
 // in LDS.  Tiles reach LDS through buffer-to-LDS loads issued three tiles
@@ -45,6 +45,8 @@
 namespace cpattn {
 
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Keep a value's computation above this point: the empty volatile statement
 // reads and rewrites the registers, so the instructions that produce them
@@ -221,7 +223,20 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
   for (int i = 0; i < kDV / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY;  // running row max of c*s (log2 domain)
-  float l_run = 0.f;        // this lane's partial row sum (its half of the keys)
+  // row sums on v_mfma_f32_16x16x32_bf16: column n of its B operand (a P^T
+  // block) is lanes n, n+16, n+32, n+48, i.e. queries n and n+16 with both
+  // halves of their keys.  Row m of the A operand comes from lanes m, m+16,
+  // m+32, m+48; rows 0 and 8 select the lane groups of query n, rows 4 and
+  // 12 those of query n+16, so the first accumulator register of lane l
+  // holds the row sum of its own query (the others stay zero).
+  f32x4 lacc = f32x4{};
+  bf16x8 lsel;
+  {
+    const int m = lane & 15, g = lane >> 4;
+    const bool on = ((m == 0 || m == 8) && !(g & 1)) || ((m == 4 || m == 12) && (g & 1));
+    const __bf16 v = on ? (__bf16)1.0f : (__bf16)0.0f;
+    lsel = bf16x8{v, v, v, v, v, v, v, v};
+  }
   f32x16 sa[kNKB], sb[kNKB];  // score buffers of consecutive tiles
 
   auto qk = [&](int t, f32x16* sc) {
@@ -265,7 +280,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      l_run *= alpha;
+      lacc[0] *= alpha;
 #pragma unroll
       for (int d = 0; d < kDV / 32; ++d)
 #pragma unroll
@@ -273,7 +288,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   };
   // P = exp2(c*s - m), bf16, laid out as the B operand of P.V; the row sum
-  // adds the rounded probabilities, two per v_dot2 against (1, 1)
+  // adds the rounded probabilities (selector products above)
   auto probs = [&](const f32x16* scur, bf16x8* pb) {
 #pragma unroll
     for (int kb = 0; kb < kNKB; ++kb)
@@ -281,16 +296,8 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       for (int i = 0; i < 16; ++i)
         pb[kb * 2 + (i >> 3)][i & 7] =
             (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(scur[kb][i], c_log2, -m_run));
-    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    float psa = 0.f, psb = 0.f;
 #pragma unroll
-    for (int u = 0; u < BN / 16; ++u) {
-      psa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 0, 1), one2, psa, false);
-      psb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 2, 3), one2, psb, false);
-      psa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 4, 5), one2, psa, false);
-      psb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[u], pb[u], 6, 7), one2, psb, false);
-    }
-    l_run += psa + psb;
+    for (int u = 0; u < BN / 16; ++u) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pb[u], lacc, 0, 0, 0);
   };
   // O^T += V^T . P^T, V^T reads two operands ahead of their use
   auto pv = [&](int t, const bf16x8* pb) {
@@ -354,7 +361,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     tnext = tile_max(snext);
 #pragma unroll
     for (int d = 0; d < kDV / 32; ++d) pin(oacc[d]);
-    pin(l_run);
+    asm volatile("" : "+v"(lacc));
     pin(tnext);
     // tile t+2 complete for S(t+2) in the next step (tile t+3 may stay in flight)
     if (t + 3 < nkt) wait_vmcnt<kMine>();
@@ -401,7 +408,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 
   // ---- epilogue: O / l -> bf16, lse = ln2 * (m + log2 l)
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = lacc[0];
   const int qi = q0w + col;
   if (qi < S) {
     const float inv = 1.0f / l_tot;
