@@ -256,16 +256,20 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int nkt = causal ? min(nkt_all, (q0 + kBM - 1) / BN + 1) : nkt_all;
 
   // ---- tile t (K and V) lives in LDS buffer t % kStages.  A tile is kLoads
-  // buffer-to-LDS loads of 1 KB (K first, then V); wave w issues loads
-  // w, w + kWaves, ..., the same number and kinds in every wave.
-  static_assert(kLoads % kWaves == 0 && kKL % kWaves == 0, "uniform load split");
-  constexpr int kMine = kLoads / kWaves;   // loads each wave issues per tile
+  // buffer-to-LDS loads of 1 KB (K first, then V), all issued by waves
+  // 0-3 (wave w issues loads w, w + 4, ..., the same number and kinds in
+  // each).  Those waves are the older wave of each SIMD, which the
+  // arbiter favours: they reach the end of an iteration first and wait at the
+  // barrier, so the issue work costs least there.
+  constexpr int kIssuers = 4;
+  static_assert(kLoads % kIssuers == 0 && kKL % kIssuers == 0, "uniform load split");
+  constexpr int kMine = kLoads / kIssuers;   // loads each issuing wave issues per tile
   uint32_t go[kMine];  // global offset inside the tile (0xfffffff0: padding, reads zeros)
   int lo_[kMine];      // LDS offset inside the stage (K region, then V region)
 #pragma unroll
   for (int i = 0; i < kMine; ++i) {
-    const int j = wave + i * kWaves;
-    if (i * kWaves < kKL) {  // the same kind of load for every wave
+    const int j = wave % kIssuers + i * kIssuers;
+    if (i * kIssuers < kKL) {  // the same kind of load for every wave
       const int row = j * kKRowsPerLoad + lane / LY::kKC;
       const int lc = (lane % LY::kKC) ^ LY::k_swz(row);  // logical chunk held by this slot
       go[i] = lc * 16 < DQK ? (uint32_t)row * rsQK + h * DQK + lc * 16 : 0xfffffff0u;
@@ -281,9 +285,10 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   auto issue_tile = [&](int t) {
     const int buf = t % LY::kStages;
     const uint32_t kb = (uint32_t)(t * BN) * rsQK, vb = (uint32_t)(t * BN) * rsV;
+    if (wave >= kIssuers) return;  // waves 4-7 have no loads (their vmcnt waits are no-ops)
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
-      if (i * kWaves < kKL)
+      if (i * kIssuers < kKL)
         buffer_load_lds16(rk, &sm.k[buf][lo_[i]], go[i] == 0xfffffff0u ? go[i] : kb + go[i]);
       else
         buffer_load_lds16(rv, &sm.v[buf][lo_[i]], vb + go[i]);
@@ -474,10 +479,17 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     // tile t+3 goes to the buffer of tile t-1, finished before the last barrier
     const bool more = t + 3 < nkt;
     if (more) issue_tile(t + 3);
+    // Wave priority 1 for the first half, 0 for the second: the two waves of
+    // a SIMD start the iteration together after the barrier, and the one
+    // that gets ahead drops below the other once it reaches P.V, so the
+    // arbiter (which otherwise favours the older wave throughout) lets the
+    // lagging wave catch up before the next barrier.
+    __builtin_amdgcn_s_setprio(1);
     refresh(bcur);
     int pscale;
     const i32x8 pw = probs(scur, bcur, pscale);
     qk(t + 1, snext);
+    __builtin_amdgcn_s_setprio(0);
     pv(t, pw, pscale);
     bnext = tile_max(snext);
 #pragma unroll
