@@ -113,8 +113,12 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   constexpr int kKL = BN / kKRowsPerLoad;          // 1 KB loads of K per tile
   constexpr int kVL = BN / 4;                      // 1 KB loads of V per tile
   constexpr int kLoads = kKL + kVL;
-  static_assert(kLoads % kWaves == 0 && kKL % kWaves == 0, "uniform load split");
-  constexpr int kMine = kLoads / kWaves;           // loads each wave issues per tile
+  // the loads of a tile are issued by waves 0-3, the older wave of each
+  // SIMD, which the arbiter favours: they reach the barrier first, so the
+  // issue work costs least there
+  constexpr int kIssuers = 4;
+  static_assert(kLoads % kIssuers == 0 && kKL % kIssuers == 0, "uniform load split");
+  constexpr int kMine = kLoads / kIssuers;           // loads each issuing wave issues per tile
   using SM = Smem<DQK, BN>;
   __shared__ __attribute__((aligned(1024))) SM sm;
 
@@ -161,13 +165,13 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int nkt = causal ? min(nkt_all, (q0 + kBM - 1) / BN + 1) : nkt_all;
 
   // ---- tile t lives in LDS stage t % kStages: kLoads buffer-to-LDS loads of
-  // 1 KB (K first, then V); wave w issues loads w, w + 8, ...
+  // 1 KB (K first, then V); wave w < 4 issues loads w, w + 4, ...
   uint32_t go[kMine];  // global offset inside the tile (0xfffffff0: padding, reads zeros)
   int lo_[kMine];      // LDS offset inside the stage (K region, then V region)
 #pragma unroll
   for (int i = 0; i < kMine; ++i) {
-    const int j = wave + i * kWaves;
-    if (i * kWaves < kKL) {  // the same kind of load for every wave
+    const int j = wave % kIssuers + i * kIssuers;
+    if (i * kIssuers < kKL) {  // the same kind of load for every wave
       const int row = j * kKRowsPerLoad + lane / LY::kKC;
       const int lc = (lane % LY::kKC) ^ (row & 15);  // logical chunk held by this slot
       go[i] = lc * 16 < DQK * 2 ? (uint32_t)row * rsQK + h * DQK * 2 + lc * 16 : 0xfffffff0u;
@@ -184,9 +188,10 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   auto issue_tile = [&](int t) {
     const int st = t % kStages;
     const uint32_t kb0 = (uint32_t)(t * BN) * rsQK, vb0 = (uint32_t)(t * BN) * rsV;
+    if (wave >= kIssuers) return;  // waves 4-7 have no loads (their vmcnt waits are no-ops)
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
-      if (i * kWaves < kKL)
+      if (i * kIssuers < kKL)
         buffer_load_lds16(rk, &sm.k[st][lo_[i]], go[i] == 0xfffffff0u ? go[i] : kb0 + go[i]);
       else
         buffer_load_lds16(rv, &sm.v[st][lo_[i]], vb0 + go[i]);
@@ -353,10 +358,15 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   auto fast_step = [&](int t, f32x16* scur, f32x16* snext, float tcur, float& tnext) {
     // tile t+3 goes to the stage of tile t-1, finished before the last barrier
     if (t + kAhead < nkt) issue_tile(t + kAhead);
+    // d = 192 (32-key tiles): wave priority 1 for the P half and 0 for the
+    // P.V half, so that the wave of a SIMD that gets ahead yields to the
+    // other before the barrier (measured neutral to negative at d = 128)
+    if constexpr (DQK == 192) __builtin_amdgcn_s_setprio(1);
     refresh(tcur);
     bf16x8 pb[BN / 16];
     probs(scur, pb);
     qk(t + 1, snext);
+    if constexpr (DQK == 192) __builtin_amdgcn_s_setprio(0);
     pv(t, pb);
     tnext = tile_max(snext);
 #pragma unroll
