@@ -125,7 +125,11 @@ struct Layout {
   static constexpr int kKPitch = kKC * 16;
   static constexpr int kKBytes = BN * kKPitch;
   static constexpr int kVBytes = BN * kDV;
-  static constexpr int kStages = 4;
+  // d = 128: eight stages and a workgroup barrier after every second tile
+  // (tiles t+4, t+5 issued together at even t); d = 192 (24 KB per stage):
+  // four stages and a barrier per tile (tile t+3 issued at t)
+  static constexpr bool kPair = DQK == 128;
+  static constexpr int kStages = kPair ? 8 : 4;
   __device__ static int k_swz(int row) { return DQK == 128 ? (row >> 1) & 7 : row & 15; }
 };
 
@@ -457,15 +461,46 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   // ---- prologue: tiles 0..2 issued, 0 and 1 complete, S(0) and its max
   float bmax_a = 0.0f, bmax_b = 0.0f;  // tile maxima of the two score buffers
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
+  for (int t = 0; t < (LY::kPair ? 4 : 3); ++t)
     if (t < nkt) issue_tile(t);
-  if (nkt > 2) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
+  // tiles 0..2 (pairs) or 0..1 complete; the last issued may stay in flight
+  if (nkt > (LY::kPair ? 3 : 2)) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
   barrier_nofence();
   if (active(0)) {
     qk(0, sa);
     if (masked(0)) apply_mask(0, sa);
     bmax_a = tile_max(sa);
   }
+
+  // Loads ahead and barriers.  Per tile: tile t+3 goes to the stage of tile
+  // t-1, finished before the last barrier; after the iteration each wave
+  // waits for its own loads of tile t+2 (needed for S(t+2) next), then the
+  // barrier (no fence: a release would wait for the loads of tile t+3 too).
+  // Per pair (d = 128): at even t tiles t+4 and t+5 go to the stages of
+  // tiles t-4 and t-3, finished before the last barrier (after iteration
+  // t-1); after odd t each wave waits for its loads of tile t+3 (needed for
+  // S(t+3) in iteration t+2, before the next barrier) and the barrier.
+  auto issue_ahead = [&](int t) {
+    if constexpr (LY::kPair) {
+      if (!(t & 1)) {
+        if (t + 4 < nkt) issue_tile(t + 4);
+        if (t + 5 < nkt) issue_tile(t + 5);
+      }
+    } else {
+      if (t + 3 < nkt) issue_tile(t + 3);
+    }
+  };
+  auto sync_after = [&](int t) {
+    if constexpr (LY::kPair) {
+      if (t & 1) {
+        if (t + 4 < nkt) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
+        barrier_nofence();
+      }
+    } else {
+      if (t + 3 < nkt) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
+      barrier_nofence();
+    }
+  };
 
   // Iteration t: P(t) from S(t) and its max, S(t+1) = K(t+1).Q^T, O += P(t).V(t),
   // then the max of S(t+1).  While tile t+1 is fully visible to every row of
@@ -476,9 +511,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   // the general form.  Every iteration ends in one workgroup barrier, so all
   // waves pass the same number of barriers.
   auto fast_step = [&](int t, f32x16* scur, f32x16* snext, float bcur, float& bnext) {
-    // tile t+3 goes to the buffer of tile t-1, finished before the last barrier
-    const bool more = t + 3 < nkt;
-    if (more) issue_tile(t + 3);
+    issue_ahead(t);
     // Wave priority 1 for the first half, 0 for the second: the two waves of
     // a SIMD start the iteration together after the barrier, and the one
     // that gets ahead drops below the other once it reaches P.V, so the
@@ -496,15 +529,10 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     for (int d = 0; d < kDV / 32; ++d) pin(oacc[d]);
     pin(l_run);
     pin(bnext);
-    // tile t+2 must be complete for S(t+2) in the next iteration: each wave
-    // waits for its own loads of it, then the barrier (no fence: a release
-    // would wait for the loads of tile t+3 as well)
-    if (more) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
-    barrier_nofence();
+    sync_after(t);
   };
   auto slow_step = [&](int t, f32x16* scur, f32x16* snext, float bcur, float& bnext) {
-    const bool more = t + 3 < nkt;
-    if (more) issue_tile(t + 3);
+    issue_ahead(t);
     if (active(t)) {
       refresh(bcur);
       int pscale;
@@ -516,8 +544,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
         bnext = tile_max(snext);
       }
     }
-    if (more) wait_vmcnt<kMine>(); else wait_vmcnt<0>();
-    barrier_nofence();
+    sync_after(t);
   };
   // first iteration whose next tile is masked: iterations below it take the
   // straight-line form (tile t+1 < nkt is then fully visible)
