@@ -58,8 +58,11 @@
 //          and the LSE carry no systematic bias; the block maximum y = 8
 //          still maps exactly to 256 (byte 0x78).
 //
-// K/V tiles pass through four LDS stages filled directly by buffer-to-LDS
-// loads issued three tiles ahead (rows past the end read as zero).
+// K/V tiles pass through LDS stages filled directly by buffer-to-LDS loads
+// issued by waves 0-3 (rows past the end read as zero): eight stages with
+// tiles t+4, t+5 issued together at even t and a barrier after every second
+// tile at d = 128, four stages with tile t+3 issued at t and a barrier per
+// tile at d = 192.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -197,8 +200,10 @@ struct Smem {
 // through the vector work of the same wave, and the other wave of the SIMD
 // fills the remaining gaps (the overlap of matrix and vector work that "Como
 // o motor de atencao FP8 da Zyphra funciona" on the miraibroadcast.com page
-// describes, obtained here from instruction order inside each wave).  One
-// workgroup barrier per tile.
+// describes, obtained here from instruction order inside each wave).  A
+// wave runs the first half at priority 1 and the second at priority 0, so
+// the wave of a SIMD that gets ahead yields to the other (the arbiter
+// otherwise favours the older wave throughout and it idles at the barrier).
 template <int DQK, int BN, bool kLean, int kOcc>
 __global__ void __launch_bounds__(256 * kOcc, 1)
 attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
@@ -508,8 +513,8 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   // straight-line regions whose matrix instructions are interleaved with the
   // vector work: P(t) alongside S(t+1), and the max of S(t+1) alongside
   // O += P(t).V(t).  The remaining iterations (masked or inactive tiles) run
-  // the general form.  Every iteration ends in one workgroup barrier, so all
-  // waves pass the same number of barriers.
+  // the general form.  Barriers come after fixed iterations (every one, or
+  // every odd one with tile pairs), so all waves pass the same number.
   auto fast_step = [&](int t, f32x16* scur, f32x16* snext, float bcur, float& bnext) {
     issue_ahead(t);
     // Wave priority 1 for the first half, 0 for the second: the two waves of
