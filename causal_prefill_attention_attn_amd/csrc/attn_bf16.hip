@@ -29,11 +29,13 @@
 // products of each P^T block with a lane-group selector, fp32 accumulation).
 //
 // Schedule: eight waves per workgroup (two per SIMD) share every K/V tile
-// in LDS.  Tiles reach LDS through buffer-to-LDS loads issued three tiles
-// ahead into four stages (rows past the end read as zero), one workgroup
-// barrier per tile.  Each wave is software-pipelined one tile deep: it
-// issues the matrix instructions of S for tile t+1 before computing the
-// probabilities of tile t, so its own matrix and vector work overlap.
+// in LDS.  Tiles reach LDS through buffer-to-LDS loads issued by waves 0-3
+// three tiles ahead into four stages (rows past the end read as zero), one
+// workgroup barrier per tile.  Each wave is software-pipelined one tile deep
+// and carries the scores of the next tile and their row maximum: P(t) is
+// formed while the matrix unit computes S(t+1), and the maximum of S(t+1)
+// is taken while it runs P(t).V(t), so its own matrix and vector work
+// overlap.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
