@@ -39,8 +39,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "attn_device.h"
 #include "attn_kernels.h"
 
