@@ -60,9 +60,8 @@
 //
 // K/V tiles pass through LDS stages filled directly by buffer-to-LDS loads
 // issued by waves 0-3 (rows past the end read as zero): eight stages with
-// tiles t+4, t+5 issued together at even t and a barrier after every second
-// tile at d = 128, four stages with tile t+3 issued at t and a barrier per
-// tile at d = 192.
+// tile t+4 issued at t and a barrier after every second tile at d = 128,
+// four stages with tile t+3 issued at t and a barrier per tile at d = 192.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -128,8 +127,8 @@ struct Layout {
   static constexpr int kKPitch = kKC * 16;
   static constexpr int kKBytes = BN * kKPitch;
   static constexpr int kVBytes = BN * kDV;
-  // d = 128: eight stages and a workgroup barrier after every second tile
-  // (tiles t+4, t+5 issued together at even t); d = 192 (24 KB per stage):
+  // d = 128: eight stages, tile t+4 issued at t and a workgroup barrier
+  // after every second tile; d = 192 (24 KB per stage):
   // four stages and a barrier per tile (tile t+3 issued at t)
   static constexpr bool kPair = DQK == 128;
   static constexpr int kStages = kPair ? 8 : 4;
@@ -481,16 +480,13 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   // t-1, finished before the last barrier; after the iteration each wave
   // waits for its own loads of tile t+2 (needed for S(t+2) next), then the
   // barrier (no fence: a release would wait for the loads of tile t+3 too).
-  // Per pair (d = 128): at even t tiles t+4 and t+5 go to the stages of
-  // tiles t-4 and t-3, finished before the last barrier (after iteration
-  // t-1); after odd t each wave waits for its loads of tile t+3 (needed for
-  // S(t+3) in iteration t+2, before the next barrier) and the barrier.
+  // Per pair (d = 128): at every t tile t+4 goes to the stage of tile t-4,
+  // finished before the last barrier (after iteration t-1 or t-2); after
+  // odd t each wave waits for its loads of tile t+3 (needed for S(t+3) in
+  // iteration t+2, before the next barrier) and the barrier.
   auto issue_ahead = [&](int t) {
     if constexpr (LY::kPair) {
-      if (!(t & 1)) {
-        if (t + 4 < nkt) issue_tile(t + 4);
-        if (t + 5 < nkt) issue_tile(t + 5);
-      }
+      if (t + 4 < nkt) issue_tile(t + 4);
     } else {
       if (t + 3 < nkt) issue_tile(t + 3);
     }
