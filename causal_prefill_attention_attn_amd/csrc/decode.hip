@@ -23,10 +23,15 @@
 //
 // Inside a workgroup: 4 waves; a wave takes tiles of 16 consecutive keys
 // (tiles w, w+4, ...), which lie in one page since pages hold a multiple of
-// 16 keys and splits start at multiples of 64.  Lane group g (16 lanes) holds
-// key g of each 4-key step; its 16 lanes share the key's row, so a score is a
-// 16-lane sum (four DPP adds) and each lane keeps 8 of the 128 output values.
-// Each lane group runs its own online softmax; the 16 streams of a workgroup
+// 16 keys and splits start at multiples of 64.  The scores of a tile for the
+// G query heads of the key/value head are one 16x16 matrix-core product
+// (keys x heads, heads past G are zero columns).  In its accumulator, lane
+// group j (16 lanes) holds keys 4j .. 4j+3 of the tile and lane j*16 + g
+// holds head g, so each (lane group, head) pair runs its own online softmax
+// over its keys on the lane's four values.  The probabilities then go through
+// a wave-private LDS slot to the P.V layout, where lane group j holds the same
+// four keys' value rows and each lane 8 of the 128 output columns for every
+// head; P.V stays in fp32 on the vector ALU.  The 16 streams of a workgroup
 // are merged at the end.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -45,17 +50,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNoKeys = -1e30f;  // running max of a stream that has seen no key
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-// Sum over the 16 lanes of a row: xor 1 and xor 2 (quad permutes), then the
-// half-row and row mirrors.  Every lane ends with the same value.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
-  return x;
-}
 
 // One lane's share of a row of `d` elements: elements 8*sub .. 8*sub+7 of the
 // first 128, and for d = 192 elements 128 + 4*sub .. +3 as well, as raw words
@@ -110,38 +106,72 @@ __device__ __forceinline__ void e4m3_words(const uint32_t* w, int n, float* out)
   }
 }
 
-// e4m3 words -> bf16 pairs, element order: the scaled convert with scale 1
-// (every e4m3 value is exact in bf16).
-__device__ __forceinline__ void e4m3_to_bf16_words(const uint32_t* w, int n, uint32_t* out) {
-  for (int i = 0; i < n; ++i) {
-    out[2 * i] = __builtin_bit_cast(uint32_t,
-                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
-    out[2 * i + 1] = __builtin_bit_cast(
-        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+// A lane's quarter of a query or key row as a matrix-core operand: lane
+// group j (lanes 16j .. 16j+15) holds bytes [j, j+1) * DQK*esz/4 of the row.
+// The query (B operand) and the keys (A operand) use the same split, so every
+// element of the row meets its partner in one product.
+template <int DQK, bool kFP8>
+struct Quarter {
+  static constexpr int kWords = DQK * (kFP8 ? 1 : 2) / 16;  // 8 / 12 (e4m3), 16 / 24 (bf16)
+  uint32_t w[kWords];
+};
+
+template <int DQK, bool kFP8>
+__device__ __forceinline__ Quarter<DQK, kFP8> load_quarter(const uint8_t* row, int part) {
+  using QT = Quarter<DQK, kFP8>;
+  QT r;
+  const u32x4* src = reinterpret_cast<const u32x4*>(row + part * QT::kWords * 4);
+#pragma unroll
+  for (int i = 0; i < QT::kWords / 4; ++i) {
+    const u32x4 x = src[i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r.w[4 * i + c] = x[c];
   }
+  return r;
 }
 
-// A lane's share of a query or key row as bf16 pairs: the raw words for
-// bf16, the converted codes for e4m3.
+// S^T (16 keys x 16 heads) of one tile: the fp32 sum of the products of a
+// lane's quarter of its key row with the same quarter of its head's query,
+// over the four quarters.  Accumulator: lane l holds head l % 16 and keys
+// 4 (l / 16) + i, i = 0..3.  e4m3 uses the 16x16x128 form (a d = 192 row
+// leaves a 16-code remainder, padded with zero codes on both sides); bf16
+// the 16x16x32 form.
 template <int DQK, bool kFP8>
-struct Pairs {
-  static constexpr int kN = DQK / 32;  // bf16 pairs per lane
-  uint32_t w[kN];
-};
-template <int DQK, bool kFP8>
-__device__ __forceinline__ Pairs<DQK, kFP8> row_pairs(const RowPart<DQK, kFP8>& r) {
-  using R = RowPart<DQK, kFP8>;
-  Pairs<DQK, kFP8> p;
+__device__ __forceinline__ f32x4 tile_scores(const Quarter<DQK, kFP8>& k,
+                                             const Quarter<DQK, kFP8>& q) {
+  using QT = Quarter<DQK, kFP8>;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (kFP8) {
-    e4m3_to_bf16_words(r.a, R::kA, p.w);
-    if constexpr (R::kB > 0) e4m3_to_bf16_words(r.b, R::kB, p.w + 2 * R::kA);
+#pragma unroll
+    for (int c = 0; c < QT::kWords / 8; ++c) {
+      i32x8 a, bq;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        a[i] = (int)k.w[8 * c + i];
+        bq[i] = (int)q.w[8 * c + i];
+      }
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bq, acc, 0, 0, 0, 0, 0, 0);
+    }
+    if constexpr (QT::kWords % 8 != 0) {
+      constexpr int c0 = QT::kWords / 8 * 8;
+      i32x8 a = {0, 0, 0, 0, 0, 0, 0, 0}, bq = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = (int)k.w[c0 + i];
+        bq[i] = (int)q.w[c0 + i];
+      }
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bq, acc, 0, 0, 0, 0, 0, 0);
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < R::kA; ++i) p.w[i] = r.a[i];
-#pragma unroll
-    for (int i = 0; i < R::kB; ++i) p.w[R::kA + i] = r.b[i];
+    for (int c = 0; c < QT::kWords / 4; ++c) {
+      u32x4 a = {k.w[4 * c], k.w[4 * c + 1], k.w[4 * c + 2], k.w[4 * c + 3]};
+      u32x4 bq = {q.w[4 * c], q.w[4 * c + 1], q.w[4 * c + 2], q.w[4 * c + 3]};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, bq), acc, 0, 0, 0);
+    }
   }
-  return p;
+  return acc;
 }
 
 template <int DQK, bool kFP8>
@@ -186,13 +216,13 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int Hq = Hkv * G;
   const int ps = 1 << ps_log2;
 
-  // the G query rows as bf16 pairs: scores are dot2 sums of pairs in fp32
-  using QP = Pairs<DQK, kFP8>;
-  QP qp[G];
+  // B operand: column sub is query head hk*G + sub, a zero column for sub >= G
+  using QT = Quarter<DQK, kFP8>;
+  QT qq = load_quarter<DQK, kFP8>(q + ((int64_t)b * Hq + hk * G + (sub < G ? sub : 0)) * DQK * esz,
+                                  grp);
+  if (sub >= G) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint8_t* qrow = q + ((int64_t)b * Hq + hk * G + g) * DQK * esz;
-    qp[g] = row_pairs<DQK, kFP8>(load_row<DQK, kFP8>(qrow, sub));
+    for (int i = 0; i < QT::kWords; ++i) qq.w[i] = 0u;
   }
 
   const int64_t rsK = (int64_t)Hkv * DQK * esz;  // bytes between slots
@@ -202,68 +232,70 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int32_t* trow = table + (int64_t)b * maxp;
 
   struct Tile {
-    RowPart<DQK, kFP8> k[4];
-    RowPart<128, kFP8> v[4];
+    QT k;                      // key row sub of the tile, quarter grp
+    RowPart<128, kFP8> v[4];   // value rows 4*grp + r, columns 8*sub .. 8*sub+7
   };
-  // rows of tile t: keys key0 + 4r + grp; keys at or past k1 read the tile's
-  // first row (a valid key) and are masked below
+  // keys at or past k1 read the tile's first row (a valid key) and are
+  // masked below
   auto load_tile = [&](int t) {
     Tile x;
     const int key0 = k0 + t * kTile;
     int page = trow[key0 >> ps_log2];
     page = page < 0 ? 0 : (page >= npages ? npages - 1 : page);
     const int64_t slot0 = (int64_t)page * ps + (key0 & (ps - 1));
+    x.k = load_quarter<DQK, kFP8>(kbase + (slot0 + (key0 + sub < k1 ? sub : 0)) * rsK, grp);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int dk = 4 * r + grp;
-      const int64_t slot = slot0 + (key0 + dk < k1 ? dk : 0);
-      x.k[r] = load_row<DQK, kFP8>(kbase + slot * rsK, sub);
-      x.v[r] = load_row<128, kFP8>(vbase + slot * rsV, sub);
+      const int dk = 4 * grp + r;
+      x.v[r] = load_row<128, kFP8>(vbase + (slot0 + (key0 + dk < k1 ? dk : 0)) * rsV, sub);
     }
     return x;
   };
 
-  float m[G], l[G], o[G][8];
+  // softmax stream of (lane group grp, head sub): keys 4*grp .. 4*grp+3 of
+  // every tile, in log2 units (meaningful for sub < G)
+  float m_s = kNoKeys, l_s = 0.0f;
+  float o[G][8];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNoKeys;
-    l[g] = 0.0f;
+  for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[g][e] = 0.0f;
-  }
+
+  // wave-private exchange slots: lane l's four probabilities and its rescale
+  // factor.  Only this wave touches them, and a wave's LDS accesses complete
+  // in order, so no workgroup barrier is needed.
+  __shared__ f32x4 sP[kWaves][64];
+  __shared__ float sA[kWaves][64];
 
   // one tile: scores, online softmax update, P.V
   auto process = [&](const Tile& x, int t) {
     const int key0 = k0 + t * kTile;
-    float sc[4][G];  // logits in log2 units, then probabilities
+    const f32x4 acc = tile_scores<DQK, kFP8>(x.k, qq);
+    f32x4 p;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool valid = key0 + 4 * r + grp < k1;
-      const QP kp = row_pairs<DQK, kFP8>(x.k[r]);
+    for (int i = 0; i < 4; ++i) p[i] = key0 + 4 * grp + i < k1 ? acc[i] * c_log2 : -INFINITY;
+    const float mx = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+    const float mn = fmaxf(m_s, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_s - mn);
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < QP::kN; ++i)
-          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qp[g].w[i]),
-                                                __builtin_bit_cast(bf16x2, kp.w[i]), acc, false);
-        acc = row16_sum(acc) * c_log2;
-        sc[r][g] = valid ? acc : -INFINITY;
-      }
-    }
-    float alpha[G];
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(p[i] - mn);
+    l_s = fmaf(l_s, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+    m_s = mn;
+    sP[wave][lane] = p;
+    sA[wave][lane] = alpha;
+    __builtin_amdgcn_wave_barrier();
+    f32x4 pg[G];
+    float al[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float mx = fmaxf(fmaxf(sc[0][g], sc[1][g]), fmaxf(sc[2][g], sc[3][g]));
-      const float mn = fmaxf(m[g], mx);
-      alpha[g] = __builtin_amdgcn_exp2f(m[g] - mn);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r][g] = __builtin_amdgcn_exp2f(sc[r][g] - mn);
-      l[g] = fmaf(l[g], alpha[g], (sc[0][g] + sc[1][g]) + (sc[2][g] + sc[3][g]));
-      m[g] = mn;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] *= alpha[g];
+      pg[g] = sP[wave][16 * grp + g];
+      al[g] = sA[wave][16 * grp + g];
     }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[g][e] *= al[g];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float vv[8];
@@ -271,7 +303,7 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] = fmaf(sc[r][g], vv[e], o[g][e]);
+        for (int e = 0; e < 8; ++e) o[g][e] = fmaf(pg[g][r], vv[e], o[g][e]);
     }
   };
 
@@ -298,6 +330,18 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       // lengthens register live ranges
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  // each lane of group grp takes the stream state of its group's G heads
+  float m[G], l[G];
+  __builtin_amdgcn_wave_barrier();
+  sP[wave][lane] = f32x4{m_s, l_s, 0.0f, 0.0f};
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const f32x4 st = sP[wave][16 * grp + g];
+    m[g] = st[0];
+    l[g] = st[1];
   }
 
   // merge the four lane groups of the wave (lanes sub, sub+16, sub+32, sub+48
