@@ -10,10 +10,12 @@
 // G = H_q / H_kv.
 //
 // One query row per head makes this a matrix-vector product: 2 FLOPs per
-// cached element (G per element with grouped heads), far below the matrix
-// cores' ridge, so the kernel is bound by HBM and runs on the vector ALU in
-// fp32.  What matters is streaming the cache with wide, coalesced loads and
-// enough workgroups in flight.
+// cached element (2G with G grouped query heads per key/value head), far
+// below the matrix cores' ridge, so the kernel is bound by HBM: what matters
+// is streaming the cache with wide, coalesced loads and enough workgroups in
+// flight.  The scores of the G heads still go to the matrix cores: on the
+// vector ALU, their dot products, lane sums and a softmax repeated in every
+// lane of a key row cost more time than the memory at G = 4.
 //
 // Split over keys.  Workgroup (split s, key/value head hk, sequence b) takes
 // keys [s*split, min((s+1)*split, L)) for the G query heads of hk, and leaves
