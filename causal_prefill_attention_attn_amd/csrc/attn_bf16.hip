@@ -128,11 +128,8 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int col = lane & 31;  // query column / key row / value column inside a 32-block
   const int half = lane >> 5;
 
-  // longest-first order: the last query blocks (most keys) are issued first;
-  // all blocks of one (b, h) are H*B apart in launch order
-  const int id = blockIdx.x;
-  const int qb = nqb - 1 - id / BH;
-  const int bh = id % BH;
+  int qb, bh;
+  block_order(blockIdx.x, nqb, BH, qb, bh);
   const int b = bh / H;
   const int h = bh % H;
   // rows of this problem (a batch entry or a packed sequence); S is its length

@@ -228,9 +228,8 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  const int id = blockIdx.x;
-  const int qb = nqb - 1 - id / BH;  // longest rows first
-  const int bh = id % BH;
+  int qb, bh;
+  block_order(blockIdx.x, nqb, BH, qb, bh);
   const int b = bh / H;
   const int h = bh % H;
   // rows of this problem (a batch entry or a packed sequence); S is its length
