@@ -19,7 +19,8 @@ import os
 
 __all__ = [
     "ATTN_DTYPE_BF16", "ATTN_DTYPE_FP8", "AttnError", "lib_path", "load_library",
-    "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_amax_f32", "attn_quantize_e4m3", "attn_status_string",
+    "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_amax_f32", "attn_quantize_e4m3",
+    "attn_quantize_fp8", "attn_status_string",
     "attn_version", "attn_hadamard_f32", "attn_hadamard_bf16", "attn_hadamard_amax_f32",
     "attn_hadamard_quantize_e4m3", "attn_decode_paged", "attn_decode_workspace_bytes",
     "flash_attn_func", "flash_attn_varlen_func", "flash_attn_decode_paged", "quantize_fp8",
@@ -73,6 +74,8 @@ def load_library():
     lib.attn_amax_f32.argtypes = [vp, i64, vp, vp]
     lib.attn_quantize_e4m3.restype = i32
     lib.attn_quantize_e4m3.argtypes = [vp, i64, f32, vp, vp]
+    lib.attn_quantize_fp8.restype = i32
+    lib.attn_quantize_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     lib.attn_hadamard_f32.restype = i32
     lib.attn_hadamard_f32.argtypes = [vp, i64, i32, vp, vp]
     lib.attn_hadamard_bf16.restype = i32
@@ -129,6 +132,10 @@ def attn_quantize_e4m3(x, n, descale, out, stream=None) -> int:
     return int(load_library().attn_quantize_e4m3(x, n, descale, out, stream))
 
 
+def attn_quantize_fp8(x, rows, d, rotate, codes, descale, stream=None) -> int:
+    return int(load_library().attn_quantize_fp8(x, rows, d, rotate, codes, descale, stream))
+
+
 def attn_hadamard_f32(x, rows, d, y, stream=None) -> int:
     return int(load_library().attn_hadamard_f32(x, rows, d, y, stream))
 
@@ -175,6 +182,20 @@ def _check(status: int, where: str):
         raise AttnError(status, where)
 
 
+def _check_buffer(name, t, shape, dtype, device):
+    """A caller-supplied output buffer must be exactly what the C function
+    writes: the library cannot see buffer sizes, so a wrong one would be
+    written out of bounds."""
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
 def _element_dtype(t) -> int:
     torch = _torch()
     if t.dtype == torch.bfloat16:
@@ -211,14 +232,20 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_d
     if tuple(k.shape) != (B, S, H, d_qk) or tuple(v.shape[:3]) != (B, S, H):
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
                                                              tuple(v.shape)))
+    for name, t in (("k", k), ("v", v)):
+        if t.device != q.device:
+            raise ValueError("%s must be on %s, got %s" % (name, q.device, t.device))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d_qk)
     if out is None:
         out = torch.empty((B, S, H, d_v), dtype=torch.bfloat16, device=q.device)
+    _check_buffer("out", out, (B, S, H, d_v), torch.bfloat16, q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     if not return_lse:
         lse = None
+    if lse is not None:
+        _check_buffer("lse", lse, (B, H, S), torch.float32, q.device)
     st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                      lse.data_ptr() if lse is not None else None, B, S, H, d_qk, d_v,
                      float(softmax_scale), int(bool(causal)), dt, float(q_descale),
@@ -252,14 +279,20 @@ def flash_attn_varlen_func(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, 
     if tuple(k.shape) != (total, H, d_qk) or tuple(v.shape[:2]) != (total, H):
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
                                                              tuple(v.shape)))
+    for name, t in (("k", k), ("v", v), ("cu_seqlens", cu_seqlens)):
+        if t.device != q.device:
+            raise ValueError("%s must be on %s, got %s" % (name, q.device, t.device))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d_qk)
     if out is None:
         out = torch.empty((total, H, d_v), dtype=torch.bfloat16, device=q.device)
+    _check_buffer("out", out, (total, H, d_v), torch.bfloat16, q.device)
     if return_lse and lse is None:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
     if not return_lse:
         lse = None
+    if lse is not None:
+        _check_buffer("lse", lse, (H, total), torch.float32, q.device)
     st = attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                          lse.data_ptr() if lse is not None else None, cu_seqlens.data_ptr(),
                          cu_seqlens.numel() - 1, total, int(max_seqlen), H, d_qk, d_v,
@@ -304,18 +337,30 @@ def flash_attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seql
         raise ValueError("shape mismatch: q %s k_cache %s v_cache %s block_table %s seq_lens %s"
                          % (tuple(q.shape), tuple(k_cache.shape), tuple(v_cache.shape),
                             tuple(block_table.shape), tuple(seq_lens.shape)))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens)):
+        if t.device != q.device:
+            raise ValueError("%s must be on %s, got %s" % (name, q.device, t.device))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d_qk)
     need = attn_decode_workspace_bytes(B, H_q, H_kv, int(max_seqlen), d_v)
     _check(need if need < 0 else 0, "attn_decode_workspace_bytes")
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or workspace.dtype != torch.uint8 or workspace.dim() != 1 \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor on %s" % q.device)
+    if workspace.numel() < need:
+        raise ValueError("workspace holds %d bytes, the call needs %d" % (workspace.numel(), need))
     if out is None:
         out = torch.empty((B, H_q, d_v), dtype=torch.bfloat16, device=q.device)
+    _check_buffer("out", out, (B, H_q, d_v), torch.bfloat16, q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
     if not return_lse:
         lse = None
+    if lse is not None:
+        _check_buffer("lse", lse, (B, H_q), torch.float32, q.device)
     st = attn_decode_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                            block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                            lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
@@ -328,34 +373,23 @@ def flash_attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seql
 
 
 def quantize_fp8(x, rotate=False):
-    """Per-tensor E4M3FN quantization on the GPU: returns (codes uint8, descale)
-    with descale = amax / 448 computed in fp32 (1.0 for an all-zero tensor).
-    With ``rotate`` the rows of the last dimension (128 or 192) are rotated by
-    the Hadamard matrix H first (as ``hadamard``), inside the quantization
-    passes: the codes are those of x . H."""
+    """Per-tensor E4M3FN quantization on the GPU (attn_quantize_fp8): returns
+    (codes uint8, descale), descale = amax / 448 in fp32 (1.0 for an
+    all-zero tensor), both computed by the library on the device; the descale
+    is then copied to the host for the attention call.  With ``rotate`` the
+    rows of the last dimension (128 or 192) are rotated by the Hadamard matrix
+    H first (as ``hadamard``), inside the quantization passes: the codes are
+    those of x . H."""
     torch = _torch()
-    import numpy as np
-    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or x.dim() < 1:
         raise ValueError("x must be a contiguous float32 CUDA tensor")
-    n = x.numel()
-    st = _stream_handle(x.device)
-    amax = torch.empty((1,), dtype=torch.float32, device=x.device)
-    if rotate:
-        d = x.shape[-1]
-        _check(attn_hadamard_amax_f32(x.data_ptr(), n // d, d, amax.data_ptr(), st),
-               "attn_hadamard_amax_f32")
-    else:
-        _check(attn_amax_f32(x.data_ptr(), n, amax.data_ptr(), st), "attn_amax_f32")
-    a = np.float32(amax.item())
-    descale = float(a / np.float32(448.0)) if a > 0 else 1.0
+    d = x.shape[-1]
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    if rotate:
-        _check(attn_hadamard_quantize_e4m3(x.data_ptr(), n // d, d, descale, codes.data_ptr(), st),
-               "attn_hadamard_quantize_e4m3")
-    else:
-        _check(attn_quantize_e4m3(x.data_ptr(), n, descale, codes.data_ptr(), st),
-               "attn_quantize_e4m3")
-    return codes, descale
+    descale = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _check(attn_quantize_fp8(x.data_ptr(), x.numel() // max(d, 1), d, int(bool(rotate)),
+                             codes.data_ptr(), descale.data_ptr(), _stream_handle(x.device)),
+           "attn_quantize_fp8")
+    return codes, float(descale.item())
 
 
 def hadamard(x, out=None):

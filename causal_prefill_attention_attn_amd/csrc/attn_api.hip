@@ -151,6 +151,22 @@ int attn_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out, v
              : ATTN_ERR_LAUNCH;
 }
 
+int attn_quantize_fp8(const float* x, int64_t rows, int d, int rotate, uint8_t* codes,
+                      float* descale, void* stream) {
+  if (!x || !codes || !descale) return ATTN_ERR_NULL;
+  if (rows < 1 || d < 1 || rows > INT64_MAX / ((int64_t)d * 4)) return ATTN_ERR_SHAPE;
+  if (rotate != 0 && rotate != 1) return ATTN_ERR_UNSUPPORTED;
+  if (rotate && d != 128 && d != 192) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned(x, 4) || !aligned(descale, 4)) return ATTN_ERR_ALIGN;
+  const int64_t n = rows * d;
+  if (overlap(codes, n, x, n * 4) || overlap(descale, 4, x, n * 4) || overlap(descale, 4, codes, n))
+    return ATTN_ERR_ALIAS;
+  return cpattn::launch_quantize_fp8(x, rows, d, rotate != 0, codes, descale,
+                                     reinterpret_cast<hipStream_t>(stream)) == 0
+             ? ATTN_OK
+             : ATTN_ERR_LAUNCH;
+}
+
 }  // extern "C"
 
 namespace {

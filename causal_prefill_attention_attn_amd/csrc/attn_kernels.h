@@ -35,6 +35,14 @@ int launch_hadamard_amax(const float* x, int64_t rows, int d, float* amax_out,
                          hipStream_t stream);
 int launch_hadamard_quantize(const float* x, int64_t rows, int d, float descale, uint8_t* out,
                              hipStream_t stream);
+// the same with the descale read from device memory
+int launch_hadamard_quantize_dev(const float* x, int64_t rows, int d, const float* descale,
+                                 uint8_t* out, hipStream_t stream);
+// Whole per-tensor quantization on the device: amax (of the rotated rows when
+// rotate, d in {128, 192}), descale = amax / 448 (1 when zero) written to
+// *descale, then the codes of x / descale.
+int launch_quantize_fp8(const float* x, int64_t rows, int d, bool rotate, uint8_t* codes,
+                        float* descale, hipStream_t stream);
 
 // Decode step against a paged KV cache (decode.hip).  split/nsplit come from
 // decode_split_policy; the workspace holds B*Hq*nsplit partial outputs of 128

@@ -26,7 +26,7 @@ namespace {
 
 // Rotated row r of x into v (lane l holds elements l, l + 64, ...)
 template <int D, bool kBF16>
-__device__ __forceinline__ void rotate_row(const void* __restrict__ x, int64_t r, int lane,
+__device__ __forceinline__ void rotate_row(const void* x, int64_t r, int lane,
                                            float (&v)[D / 64]) {
   constexpr int J = D / 64;
   constexpr float kNorm = D == 128 ? 0.088388347648318440550f : 0.125f;  // 1/sqrt(block)
@@ -54,9 +54,11 @@ __device__ __forceinline__ void rotate_row(const void* __restrict__ x, int64_t r
   for (int j = 0; j < J; ++j) v[j] *= kNorm;
 }
 
+// x and y may be the same buffer (an in-place rotation): each wave reads its
+// whole row into registers before it writes that row, and rows are disjoint
+// between waves, so neither pointer is declared __restrict__.
 template <int D, bool kBF16>
-__global__ void __launch_bounds__(256) hadamard_kernel(const void* __restrict__ x, int64_t rows,
-                                                       void* __restrict__ y) {
+__global__ void __launch_bounds__(256) hadamard_kernel(const void* x, int64_t rows, void* y) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
   for (int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows;
@@ -98,11 +100,15 @@ __global__ void __launch_bounds__(256) hadamard_amax_kernel(const float* __restr
   if (threadIdx.x == 0) atomicMax(out, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
 }
 
-// e4m3 codes of the rotated rows divided by descale
+// e4m3 codes of the rotated rows divided by descale (read from device memory
+// when dptr is set, else the argument)
 template <int D>
 __global__ void __launch_bounds__(256) hadamard_quantize_kernel(const float* __restrict__ x,
-                                                                int64_t rows, float descale,
+                                                                int64_t rows,
+                                                                const float* __restrict__ dptr,
+                                                                float dval,
                                                                 uint8_t* __restrict__ out) {
+  const float descale = dptr != nullptr ? *dptr : dval;
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
   for (int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); r < rows;
@@ -145,14 +151,28 @@ int launch_hadamard_amax(const float* x, int64_t rows, int d, float* amax_out,
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_hadamard_quantize(const float* x, int64_t rows, int d, float descale, uint8_t* out,
-                             hipStream_t stream) {
+namespace {
+int hadamard_quantize(const float* x, int64_t rows, int d, const float* dptr, float dval,
+                      uint8_t* out, hipStream_t stream) {
   const dim3 grid(hadamard_grid(rows)), block(256);
   if (d == 128)
-    hipLaunchKernelGGL(hadamard_quantize_kernel<128>, grid, block, 0, stream, x, rows, descale, out);
+    hipLaunchKernelGGL(hadamard_quantize_kernel<128>, grid, block, 0, stream, x, rows, dptr, dval,
+                       out);
   else
-    hipLaunchKernelGGL(hadamard_quantize_kernel<192>, grid, block, 0, stream, x, rows, descale, out);
+    hipLaunchKernelGGL(hadamard_quantize_kernel<192>, grid, block, 0, stream, x, rows, dptr, dval,
+                       out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+}  // namespace
+
+int launch_hadamard_quantize(const float* x, int64_t rows, int d, float descale, uint8_t* out,
+                             hipStream_t stream) {
+  return hadamard_quantize(x, rows, d, nullptr, descale, out, stream);
+}
+
+int launch_hadamard_quantize_dev(const float* x, int64_t rows, int d, const float* descale,
+                                 uint8_t* out, hipStream_t stream) {
+  return hadamard_quantize(x, rows, d, descale, 1.0f, out, stream);
 }
 
 }  // namespace cpattn

@@ -32,11 +32,26 @@ __global__ void __launch_bounds__(256) amax_kernel(const float* __restrict__ x, 
   if (threadIdx.x == 0) atomicMax(out, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
 }
 
+// descale from device memory when dptr is set (the whole quantization then
+// runs without a host round trip), else the argument
 __global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ x, int64_t n,
-                                                       float descale, uint8_t* __restrict__ out) {
+                                                       const float* __restrict__ dptr,
+                                                       float dval, uint8_t* __restrict__ out) {
+  const float descale = dptr != nullptr ? *dptr : dval;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
     out[i] = e4m3_from_f32(x[i] / descale);
+}
+
+// The per-tensor scale rule of the FP8 quantization, in place: *p holds
+// amax (as written by the amax kernels) and becomes amax / 448 in fp32, or
+// 1 for an all-zero tensor, so the largest magnitude lands on the largest
+// finite E4M3FN value, 448.
+__global__ void descale_from_amax(float* p) {
+  if (threadIdx.x == 0) {
+    const float a = *p;
+    *p = a > 0.0f ? a / 448.0f : 1.0f;
+  }
 }
 
 }  // namespace
@@ -54,8 +69,24 @@ int launch_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out,
                          hipStream_t stream) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, descale,
-                     out);
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n,
+                     (const float*)nullptr, descale, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_quantize_fp8(const float* x, int64_t rows, int d, bool rotate, uint8_t* codes,
+                        float* descale, hipStream_t stream) {
+  const int64_t n = rows * d;
+  int rc = rotate ? launch_hadamard_amax(x, rows, d, descale, stream)
+                  : launch_amax_f32(x, n, descale, stream);
+  if (rc != 0) return rc;
+  hipLaunchKernelGGL(descale_from_amax, dim3(1), dim3(64), 0, stream, descale);
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (rotate) return launch_hadamard_quantize_dev(x, rows, d, descale, codes, stream);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n,
+                     (const float*)descale, 1.0f, codes);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

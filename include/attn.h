@@ -181,6 +181,34 @@ int attn_amax_f32(const float* x, int64_t n, float* amax_out, void* stream);
 int attn_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out, void* stream);
 
 /*
+ * attn_quantize_fp8 -- the whole per-tensor FP8 quantization of one tensor,
+ * on the device, with nothing read back to the host:
+ *   amax     = max |x[i]|                 (of the rotated rows x . H when rotate)
+ *   descale  = amax / 448 in fp32, or 1 when amax = 0
+ *   codes[i] = E4M3FN(fp32(x[i] / descale)) (of (x . H)[i] when rotate)
+ * so the largest magnitude lands on 448, the largest finite E4M3FN value.
+ * The pages attribute most of the FP8 error to this rounding of Q, K and V
+ * and credit the rotation with about half of it ("Precisao, estabilidade e
+ * efeito na pratica" on the miraibroadcast.com page); amax / 448 is the
+ * plain reading of a per-tensor scale for the e4m3 format.  The rounding and
+ * saturation are those of attn_quantize_e4m3, the rotation that of
+ * attn_hadamard_f32, and the results equal attn_amax_f32 (or
+ * attn_hadamard_amax_f32) followed by attn_quantize_e4m3 (or
+ * attn_hadamard_quantize_e4m3) with that descale, bit for bit.
+ *   x        device, rows*d float32 values, row-major (NaN entries are
+ *            ignored by the amax and encode to 0x7F)
+ *   rows     >= 1;  d >= 1, and 128 or 192 when rotate = 1
+ *   rotate   0 or 1 (else ATTN_ERR_UNSUPPORTED)
+ *   codes    device, rows*d bytes (written); must not overlap x
+ *   descale  device, one float32 (written): the descale of the codes, to be
+ *            passed (by value, after a copy to the host) as the q/k/v
+ *            descale of attn_fwd; must not overlap x or codes
+ * x and descale must be 4-byte aligned.
+ */
+int attn_quantize_fp8(const float* x, int64_t rows, int d, int rotate, uint8_t* codes,
+                      float* descale, void* stream);
+
+/*
  * attn_hadamard_f32 / attn_hadamard_bf16 -- y[r,:] = x[r,:] . H for `rows`
  * rows of d elements, with H the normalized Sylvester-Hadamard matrix of
  * order 128 (d = 128) or block-diagonal with three order-64 blocks

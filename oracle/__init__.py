@@ -66,6 +66,8 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_attn_stats.restype = ctypes.c_int
+        lib.oracle_attn_stats.argtypes = lib.oracle_attn.argtypes + [ctypes.c_void_p] * 3
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -113,12 +115,17 @@ def quantize_e4m3(x: np.ndarray, descale: float) -> np.ndarray:
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: int, tau: float,
               causal: bool = True, rows=None, q_descale: float = 1.0, k_descale: float = 1.0,
-              v_descale: float = 1.0):
+              v_descale: float = 1.0, stats: bool = False):
     """fp64 attention on raw element encodings.
 
     q, k: [B,S,H,d_qk]; v: [B,S,H,d_v]; uint16 bf16 bit patterns (dtype BF16)
     or uint8 E4M3 codes (dtype FP8).  ``rows``: query rows to evaluate (all
-    when None).  Returns (o [B,len(rows),H,d_v], lse [B,H,len(rows)]) float64.
+    when None).  Returns (o [B,len(rows),H,d_v], lse [B,H,len(rows)]) float64,
+    and with ``stats`` a third item: a dict of per-row arrays [B,H,len(rows)]
+    ``kappa`` (sensitivity of the row to relative errors of its
+    probabilities), ``wmax`` (softmax mass at the row maximum) and ``sabs``
+    (softmax-weighted mean over keys of tau times the sum of |q_c k_c|), as
+    defined in attn_oracle.c.
     """
     lib = _load()
     want = np.uint16 if dtype == BF16 else np.uint8
@@ -131,12 +138,15 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: int, tau: floa
     rows = np.arange(S, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
     o = np.empty((B, rows.size, H, dv), np.float64)
     lse = np.empty((B, H, rows.size), np.float64)
-    rc = lib.oracle_attn(_ptr(q), _ptr(k), _ptr(v), dtype, q_descale, k_descale, v_descale,
-                         B, S, H, dqk, dv, float(tau), int(bool(causal)), _ptr(rows), rows.size,
-                         _ptr(o), _ptr(lse))
+    st = {n: np.empty((B, H, rows.size), np.float64) for n in ("kappa", "wmax", "sabs")} \
+        if stats else None
+    extra = [_ptr(st[n]) for n in ("kappa", "wmax", "sabs")] if stats else [None] * 3
+    rc = lib.oracle_attn_stats(_ptr(q), _ptr(k), _ptr(v), dtype, q_descale, k_descale,
+                               v_descale, B, S, H, dqk, dv, float(tau), int(bool(causal)),
+                               _ptr(rows), rows.size, _ptr(o), _ptr(lse), *extra)
     if rc != 0:
         raise ValueError("oracle_attn rejected its arguments")
-    return o, lse
+    return (o, lse, st) if stats else (o, lse)
 
 
 def decode_paged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,

@@ -148,11 +148,37 @@ static inline double elem(const void* base, int64_t idx, int dtype, double desca
 /*
  * Attention for the query rows listed in `rows` (each in [0,S)), all batches
  * and heads.  Returns 0 on success, -1 on bad arguments.
+ *
+ * Optional per-row statistics of the same softmax (each array [B,H,nrows],
+ * skipped when NULL), for judging how a row's result reacts to rounding of
+ * its probabilities, which is where a reduced-precision evaluation of the
+ * method loses accuracy (the pages round P to e4m3, "Como o motor de atencao
+ * FP8 da Zyphra funciona" on the miraibroadcast.com page, and measure the
+ * error against fp64, "Precisao, estabilidade e efeito na pratica" on the
+ * same page).  With w_ij = exp(s_ij - m_i) / l_i the softmax weights:
+ *
+ *   kappa_i = sqrt(sum_j w_ij^2 |vhat_j - o_i|^2) / |o_i|
+ *       If every weight is perturbed as w_ij (1 + e_j), with e_j independent,
+ *       zero-mean and of RMS e, and the row renormalised, then to first
+ *       order o_i moves by sum_j w_ij e_j (vhat_j - o_i), whose RMS norm is
+ *       e * kappa_i * |o_i|: kappa_i is the factor by which relative errors
+ *       of the probabilities become a relative error of the row.  0 / 0 is
+ *       taken as 0 (a single visible key, or equal value rows), x / 0 as inf.
+ *   wmax_i  = sum of w_ij over the keys whose score equals m_i (the softmax
+ *       mass at the row maximum).
+ *   sabs_i  = sum_j w_ij * |tau| * sum_c |qhat_ic * khat_jc|: the
+ *       softmax-weighted magnitude of the terms of the row's scores.  An
+ *       evaluation of a score that loses precision relative to its terms
+ *       rather than to its (possibly cancelled) value errs by a multiple of
+ *       that score's term magnitude; weighted by w_ij this bounds the
+ *       resulting first-order change of the row's log-sum-exp and scales
+ *       the resulting relative errors of its weights.
  */
-int oracle_attn(const void* q, const void* k, const void* v, int dtype, float q_descale,
-                float k_descale, float v_descale, int64_t B, int64_t S, int64_t H, int64_t d_qk,
-                int64_t d_v, double tau, int causal, const int64_t* rows, int64_t nrows, double* o,
-                double* lse) {
+int oracle_attn_stats(const void* q, const void* k, const void* v, int dtype, float q_descale,
+                      float k_descale, float v_descale, int64_t B, int64_t S, int64_t H,
+                      int64_t d_qk, int64_t d_v, double tau, int causal, const int64_t* rows,
+                      int64_t nrows, double* o, double* lse, double* kappa, double* wmax,
+                      double* sabs) {
   if (!q || !k || !v || !o || !lse || !rows) return -1;
   if (B < 1 || S < 1 || H < 1 || d_qk < 1 || d_v < 1 || nrows < 1) return -1;
   if (dtype != ORACLE_BF16 && dtype != ORACLE_FP8) return -1;
@@ -196,13 +222,52 @@ int oracle_attn(const void* q, const void* k, const void* v, int dtype, float q_
       }
       double* orow = o + ((b * nrows + r) * H + h) * d_v;
       for (int64_t c = 0; c < d_v; ++c) orow[c] = acc[c] / l;
-      lse[(b * H + h) * nrows + r] = m + log(l);
+      const int64_t srow = (b * H + h) * nrows + r;
+      lse[srow] = m + log(l);
+      if (kappa) {
+        double num = 0.0, den = 0.0;
+        for (int64_t c = 0; c < d_v; ++c) den += orow[c] * orow[c];
+        for (int64_t j = 0; j < nvis; ++j) {
+          const double w = exp(s[j] - m) / l;
+          const int64_t vb = ((b * S + j) * H + h) * d_v;
+          double dist = 0.0;
+          for (int64_t c = 0; c < d_v; ++c) {
+            const double e = elem(v, vb + c, dtype, dv) - orow[c];
+            dist += e * e;
+          }
+          num += w * w * dist;
+        }
+        kappa[srow] = num == 0.0 ? 0.0 : (den == 0.0 ? INFINITY : sqrt(num) / sqrt(den));
+      }
+      if (wmax) {
+        int64_t at_max = 0;
+        for (int64_t j = 0; j < nvis; ++j) at_max += s[j] == m;
+        wmax[srow] = (double)at_max / l;
+      }
+      if (sabs) {
+        double acc_w = 0.0;
+        for (int64_t j = 0; j < nvis; ++j) {
+          const int64_t kb = ((b * S + j) * H + h) * d_qk;
+          double a = 0.0;
+          for (int64_t c = 0; c < d_qk; ++c) a += fabs(qi[c] * elem(k, kb + c, dtype, dk));
+          acc_w += exp(s[j] - m) / l * fabs(tau) * a;
+        }
+        sabs[srow] = acc_w;
+      }
     }
     free(s);
     free(qi);
     free(acc);
   }
   return 0;
+}
+
+int oracle_attn(const void* q, const void* k, const void* v, int dtype, float q_descale,
+                float k_descale, float v_descale, int64_t B, int64_t S, int64_t H, int64_t d_qk,
+                int64_t d_v, double tau, int causal, const int64_t* rows, int64_t nrows, double* o,
+                double* lse) {
+  return oracle_attn_stats(q, k, v, dtype, q_descale, k_descale, v_descale, B, S, H, d_qk, d_v,
+                           tau, causal, rows, nrows, o, lse, NULL, NULL, NULL);
 }
 
 /* Number of threads the parallel regions above use (for reporting). */

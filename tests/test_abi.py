@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["attn_version", "attn_status_string", "attn_fwd", "attn_fwd_ex",
                             "attn_fwd_varlen",
-                            "attn_amax_f32",
+                            "attn_amax_f32", "attn_quantize_fp8",
                             "attn_quantize_e4m3", "attn_hadamard_f32", "attn_hadamard_bf16",
                             "attn_hadamard_amax_f32", "attn_hadamard_quantize_e4m3",
                             "attn_decode_paged", "attn_decode_workspace_bytes"]), names
@@ -97,6 +97,24 @@ def test_quant_entry_points_reject(lib):
     assert pkg.attn_quantize_e4m3(Q, 10, 1.0, None) == -1
     assert pkg.attn_quantize_e4m3(Q, 0, 1.0, O) == -2
     assert pkg.attn_quantize_e4m3(Q, 16, 1.0, Q + 8) == -7
+
+
+def test_quantize_fp8_rejects(lib):
+    D = 0x68000000   # descale slot
+    f = pkg.attn_quantize_fp8
+    assert f(None, 4, 128, 0, O, D) == -1
+    assert f(Q, 4, 128, 0, None, D) == -1
+    assert f(Q, 4, 128, 0, O, None) == -1
+    assert f(Q, 0, 128, 0, O, D) == -2
+    assert f(Q, 4, 0, 0, O, D) == -2
+    assert f(Q, 1 << 60, 128, 0, O, D) == -2
+    assert f(Q, 4, 128, 2, O, D) == -4            # rotate is 0 or 1
+    assert f(Q, 4, 100, 1, O, D) == -4            # rotation needs rows of 128 or 192
+    assert f(Q + 2, 4, 128, 0, O, D) == -6
+    assert f(Q, 4, 128, 0, O, D + 2) == -6
+    assert f(Q, 4, 128, 0, Q + 100, D) == -7      # codes inside x
+    assert f(Q, 4, 128, 0, O, Q + 64) == -7       # descale inside x
+    assert f(Q, 4, 128, 0, O, O + 8) == -7        # descale inside the codes
 
 
 def test_hadamard_entry_points_reject(lib):

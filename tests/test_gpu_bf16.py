@@ -102,8 +102,8 @@ def test_c2_full_size_sampled_rows(oracle):
     print("case C2", flush=True)
     enc, ds, dev = make_inputs(oracle, w)
     o, lse = run_gpu(dev, w, ds)
-    rows = synth.sample_rows(w.S, 96)
-    check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, 13, 31])
+    rows = synth.sample_rows(w.S, 256)
+    check(oracle, w, enc, ds, o, lse, rows=rows)
 
 
 def test_bad_arguments_raise():
@@ -118,13 +118,13 @@ def test_bad_arguments_raise():
 
 
 def test_c2x_full_size_sampled_rows(oracle):
-    """The BF16 workload at 32K (B1 H32 S32768): sampled rows of three heads."""
+    """The BF16 workload at 32K (B1 H32 S32768): 256 sampled rows of every head."""
     w = synth.WORKLOADS["C2x"]
     print("case C2x", flush=True)
     enc, ds, dev = make_inputs(oracle, w)
     o, lse = run_gpu(dev, w, ds)
-    rows = synth.sample_rows(w.S, 64)
-    check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, 13, 31])
+    rows = synth.sample_rows(w.S, 256)
+    check(oracle, w, enc, ds, o, lse, rows=rows)
 
 
 def test_c5b_full_size_sampled_rows(oracle):
@@ -133,5 +133,5 @@ def test_c5b_full_size_sampled_rows(oracle):
     print("case C5b", flush=True)
     enc, ds, dev = make_inputs(oracle, w)
     o, lse = run_gpu(dev, w, ds)
-    rows = synth.sample_rows(w.S, 48)
-    check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, 15])
+    rows = synth.sample_rows(w.S, 256)
+    check(oracle, w, enc, ds, o, lse, rows=rows)

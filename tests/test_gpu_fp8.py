@@ -83,12 +83,27 @@ def test_deterministic(oracle):
 
 @pytest.mark.parametrize("name", ["C3", "C4", "C4g", "C5"])
 def test_full_size_sampled_rows(oracle, name):
+    """Every head, 256 sampled rows each (first rows, tile and workgroup
+    edges, the middle, the end, seeded uniform rows), at the bench's launch
+    configuration: at 32K tokens the grid runs the XCD head-major order."""
     w = synth.WORKLOADS[name]
     print("case", name, flush=True)
     enc, ds, dev = make_inputs(oracle, w)
     o, lse = run_gpu(dev, w, ds)
-    rows = synth.sample_rows(w.S, 48)
-    check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, w.H // 2, w.H - 1])
+    rows = synth.sample_rows(w.S, 256)
+    check(oracle, w, enc, ds, o, lse, rows=rows)
+    del dev, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_two_batches_at_32k(oracle):
+    """B = 2, H = 4 at 32K tokens: B*H = 8 problems of 128 query blocks take
+    the XCD head-major grid order with a batch index above 0."""
+    w = _w("fp8_b2_32k", 2, 4, 32768, index=76)
+    print("case", w.name, flush=True)
+    enc, ds, dev = make_inputs(oracle, w)
+    o, lse = run_gpu(dev, w, ds)
+    check(oracle, w, enc, ds, o, lse, rows=synth.sample_rows(w.S, 128))
     del dev, o, lse
     torch.cuda.empty_cache()
 
@@ -108,7 +123,7 @@ def test_exact_p_ragged_lengths(oracle, S, d_qk):
     print("case", w.name, flush=True)
     enc, ds, dev = make_inputs(oracle, w)
     o, lse = _run_exact(dev, w, ds)
-    check(oracle, w, enc, ds, o, lse)
+    check(oracle, w, enc, ds, o, lse, exact_p=True)
 
 
 def test_exact_p_full_size_sampled_rows(oracle):
@@ -116,7 +131,7 @@ def test_exact_p_full_size_sampled_rows(oracle):
     print("case C4g exact P", flush=True)
     enc, ds, dev = make_inputs(oracle, w)
     o, lse = _run_exact(dev, w, ds)
-    rows = synth.sample_rows(w.S, 32)
-    check(oracle, w, enc, ds, o, lse, rows=rows, heads=[0, 31])
+    rows = synth.sample_rows(w.S, 256)
+    check(oracle, w, enc, ds, o, lse, rows=rows, exact_p=True)
     del dev, o, lse
     torch.cuda.empty_cache()

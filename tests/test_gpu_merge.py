@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from causal_prefill_attention_attn_amd import synth
-from gpu_util import TOL, LSE_REL, WORST_ROW, errors, o_to_f64, run_gpu, u8_to_device, bf16_to_device
+from gpu_util import bf16_to_device, judge, o_to_f64, run_gpu, u8_to_device
 from merge_util import merge
 
 pytestmark = pytest.mark.gpu
@@ -48,13 +48,7 @@ def test_two_key_halves_merge_to_causal_attention(oracle, dtype, d_qk):
              (o_to_f64(o_b), l_b.cpu().numpy().astype(np.float64))]
     go, gl = merge(parts)
     rows = np.arange(N, 2 * N)
-    ro, rl = oracle.attention(q, k, v, dtype, w.softmax_scale, True, rows=rows,
-                              q_descale=ds[0], k_descale=ds[1], v_descale=ds[2])
-    pooled, rms, worst = errors(go, ro)
-    lerr = float(np.abs(gl - rl).max())
-    tol = TOL[dtype]
-    msg = "merge d%d pooled %.3e row-RMS %.3e worst %.3e max|dlse| %.3e" % (d_qk, pooled, rms, worst, lerr)
-    print(msg, flush=True)
-    assert np.isfinite(go).all()
-    assert pooled <= tol and rms <= tol and worst <= WORST_ROW[dtype] * tol, msg
-    assert float((np.abs(gl - rl) - LSE_REL[dtype] * np.abs(rl)).max()) <= tol, msg
+    ro, rl, st = oracle.attention(q, k, v, dtype, w.softmax_scale, True, rows=rows,
+                                  q_descale=ds[0], k_descale=ds[1], v_descale=ds[2], stats=True)
+    # each half encodes its own maximum exactly, not necessarily the row's
+    judge("merge d%d" % d_qk, dtype, go, gl, ro, rl, st, top_exact=False)

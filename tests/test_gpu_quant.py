@@ -71,3 +71,36 @@ def test_amax_zero_and_nan(oracle):
     assert pkg.attn_amax_f32(tx.data_ptr(), x.size, out.data_ptr(), None) == 0
     torch.cuda.synchronize()
     assert float(out.item()) == 3.0
+
+
+@pytest.mark.parametrize("rotate,d", [(0, 100), (0, 128), (1, 128), (1, 192)])
+def test_quantize_fp8_entry_point(oracle, rotate, d):
+    """attn_quantize_fp8 runs the whole quantization on the device: its
+    descale is the oracle's amax/448 of the (rotated) tensor and its codes are
+    the oracle's encoding with that descale, bit for bit."""
+    rng = np.random.default_rng(123 + d + rotate)
+    x = (rng.standard_normal((777, d)) * np.exp(rng.standard_normal(d))).astype(np.float32)
+    tx = torch.from_numpy(x).to(DEV)
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+    ds = torch.empty((1,), dtype=torch.float32, device=DEV)
+    assert pkg.attn_quantize_fp8(tx.data_ptr(), 777, d, rotate, codes.data_ptr(), ds.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    if rotate:
+        # the library rotates in fp32; take its rotated tensor as the input of
+        # the oracle's codec (the rotation itself is checked against the oracle
+        # in the Hadamard tests)
+        xr = pkg.hadamard(tx).cpu().numpy()
+    else:
+        xr = x
+    ref_ds = oracle.descale_amax(xr)
+    assert np.float32(ds.item()) == np.float32(ref_ds)
+    assert np.array_equal(codes.cpu().numpy(), oracle.quantize_e4m3(xr, ref_ds))
+
+
+def test_quantize_fp8_all_zero():
+    x = torch.zeros((64, 128), dtype=torch.float32, device=DEV)
+    codes, descale = pkg.quantize_fp8(x)
+    assert descale == 1.0 and int(codes.sum()) == 0
+    codes, descale = pkg.quantize_fp8(x, rotate=True)
+    assert descale == 1.0 and int(codes.sum()) == 0
