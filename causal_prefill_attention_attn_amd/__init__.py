@@ -22,13 +22,15 @@ __all__ = [
     "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_amax_f32", "attn_quantize_e4m3",
     "attn_quantize_fp8", "attn_status_string",
     "attn_version", "attn_hadamard_f32", "attn_hadamard_bf16", "attn_hadamard_amax_f32",
-    "attn_hadamard_quantize_e4m3", "attn_decode_paged", "attn_decode_workspace_bytes",
+    "attn_hadamard_quantize_e4m3", "attn_decode_paged", "attn_decode_paged_noalloc",
+    "attn_decode_workspace_bytes", "ATTN_DECODE_SCRATCH_BYTES",
     "flash_attn_func", "flash_attn_varlen_func", "flash_attn_decode_paged", "quantize_fp8",
     "hadamard",
 ]
 
 ATTN_DTYPE_BF16 = 0
 ATTN_DTYPE_FP8 = 1
+ATTN_DECODE_SCRATCH_BYTES = 32 << 20   # include/attn.h: the static scratch of the allocation-free decode
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcpattn.so")
@@ -87,6 +89,9 @@ def load_library():
     lib.attn_decode_paged.restype = i32
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
                                       i32, i64, i64, i64, i64, f32, i32, f32, f32, f32, vp]
+    lib.attn_decode_paged_noalloc.restype = i32
+    lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
+                                              i64, i64, i64, i64, f32, i32, f32, f32, f32, vp]
     lib.attn_decode_workspace_bytes.restype = i64
     lib.attn_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     _lib = lib
@@ -161,6 +166,16 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, worksp
         q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace, workspace_bytes, B, H_q,
         H_kv, d_qk, d_v, num_pages, page_size, max_pages_per_seq, max_seqlen, softmax_scale,
         dtype, q_descale, k_descale, v_descale, stream))
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, H_q, H_kv,
+                              d_qk, d_v, num_pages, page_size, max_pages_per_seq, max_seqlen,
+                              softmax_scale, dtype, q_descale=1.0, k_descale=1.0, v_descale=1.0,
+                              stream=None) -> int:
+    return int(load_library().attn_decode_paged_noalloc(
+        q, k_cache, v_cache, block_table, seq_lens, o, lse, B, H_q, H_kv, d_qk, d_v, num_pages,
+        page_size, max_pages_per_seq, max_seqlen, softmax_scale, dtype, q_descale, k_descale,
+        v_descale, stream))
 
 
 def attn_decode_workspace_bytes(B, H_q, H_kv, max_seqlen, d_v) -> int:

@@ -38,6 +38,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIAS: return "o or lse overlaps an input or the other output";
     case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes";
+    case ATTN_ERR_SCRATCH: return "the step needs more than the library's static decode scratch (ATTN_DECODE_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -250,15 +251,20 @@ int64_t attn_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_
   return cpattn::decode_workspace_bytes(B, H_q, H_kv, max_seqlen);
 }
 
-int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
-                      void* workspace, int64_t workspace_bytes, int64_t B, int64_t H_q,
-                      int64_t H_kv, int d_qk, int d_v, int64_t num_pages, int64_t page_size,
-                      int64_t max_pages_per_seq, int64_t max_seqlen, float softmax_scale,
-                      int dtype, float q_descale, float k_descale, float v_descale,
-                      void* stream) {
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o || !workspace)
-    return ATTN_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by attn_decode_paged (caller's workspace) and
+// attn_decode_paged_noalloc (workspace null: the library's static scratch).
+int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+           const int32_t* seq_lens, void* o, float* lse, void* workspace, int64_t workspace_bytes,
+           int64_t B, int64_t H_q, int64_t H_kv, int d_qk, int d_v, int64_t num_pages,
+           int64_t page_size, int64_t max_pages_per_seq, int64_t max_seqlen,
+           float softmax_scale, int dtype, float q_descale, float k_descale, float v_descale,
+           void* stream) {
+  const bool own = workspace == nullptr;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o) return ATTN_ERR_NULL;
   int rc = decode_sizes(B, H_q, H_kv, max_seqlen, d_v);
   if (rc != ATTN_OK) return rc;
   if (page_size < 16 || page_size > ((int64_t)1 << 20) || (page_size & (page_size - 1)) != 0 ||
@@ -278,7 +284,8 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
       !aligned(workspace, 16))
     return ATTN_ERR_ALIGN;
   const int64_t need = cpattn::decode_workspace_bytes(B, H_q, H_kv, max_seqlen);
-  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (own && need > cpattn::kDecodeScratchBytes) return ATTN_ERR_SCRATCH;
+  if (!own && workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   const int64_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 1;
   const int64_t nq = B * H_q * d_qk * esz;
   const int64_t nk = num_pages * page_size * H_kv * d_qk * esz;
@@ -293,10 +300,14 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
     for (const Buf& in : inputs)
       if (overlap(out.p, out.n, in.p, in.n)) return ATTN_ERR_ALIAS;
   }
-  if ((lse && overlap(o, no, lse, nlse)) || overlap(o, no, workspace, need) ||
-      (lse && overlap(lse, nlse, workspace, need)))
+  if ((lse && overlap(o, no, lse, nlse)) || (!own && overlap(o, no, workspace, need)) ||
+      (lse && !own && overlap(lse, nlse, workspace, need)))
     return ATTN_ERR_ALIAS;
 
+  if (own) {
+    workspace = cpattn::decode_scratch();
+    if (workspace == nullptr) return ATTN_ERR_LAUNCH;
+  }
   cpattn::DecodeArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -322,6 +333,34 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   cpattn::decode_split_policy(B, H_kv, max_seqlen, &a.split, &a.nsplit);
   rc = cpattn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
   return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                      void* workspace, int64_t workspace_bytes, int64_t B, int64_t H_q,
+                      int64_t H_kv, int d_qk, int d_v, int64_t num_pages, int64_t page_size,
+                      int64_t max_pages_per_seq, int64_t max_seqlen, float softmax_scale,
+                      int dtype, float q_descale, float k_descale, float v_descale,
+                      void* stream) {
+  if (!workspace) return ATTN_ERR_NULL;
+  return decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, workspace, workspace_bytes,
+                B, H_q, H_kv, d_qk, d_v, num_pages, page_size, max_pages_per_seq, max_seqlen,
+                softmax_scale, dtype, q_descale, k_descale, v_descale, stream);
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              float* lse, int64_t B, int64_t H_q, int64_t H_kv, int d_qk, int d_v,
+                              int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                              int64_t max_seqlen, float softmax_scale, int dtype, float q_descale,
+                              float k_descale, float v_descale, void* stream) {
+  return decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, nullptr, 0, B, H_q, H_kv,
+                d_qk, d_v, num_pages, page_size, max_pages_per_seq, max_seqlen, softmax_scale,
+                dtype, q_descale, k_descale, v_descale, stream);
 }
 
 }  // extern "C"

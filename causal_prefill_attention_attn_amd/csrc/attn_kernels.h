@@ -68,4 +68,10 @@ void decode_split_policy(int64_t B, int64_t Hkv, int64_t max_seqlen, int* split,
 int64_t decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seqlen);
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Library-held decode scratch (the allocation-free entry point): its size,
+// and the current device's copy (resolved once per device), or null when the
+// runtime cannot name it.
+constexpr int64_t kDecodeScratchBytes = int64_t(32) << 20;
+void* decode_scratch();
+
 }  // namespace cpattn

@@ -39,6 +39,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -501,6 +503,34 @@ int launch_decode(const DecodeArgs& a, hipStream_t stream) {
                      opart, lpart, a.seq_lens, (__bf16*)a.o, a.lse, (int)a.Hq,
                      (int)a.max_seqlen, a.split, a.nsplit);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Scratch held by the library for callers that cannot allocate device memory
+// (attn_decode_paged_noalloc): the split partials of one decode step, up to
+// kScratchBytes.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` is a stand-in, not a device address:
+// only the address hipGetSymbolAddress returns for a device may reach a
+// kernel.  Every call on a GPU shares that GPU's copy, so calls that overlap
+// in time on one GPU race; the merge reads only partials the same step's
+// split kernel wrote, so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device, filled on the first call there
+}  // namespace
+
+void* decode_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace cpattn

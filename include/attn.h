@@ -48,6 +48,11 @@ extern "C" {
 #define ATTN_ERR_ALIAS (-7)       /* an output buffer overlaps an input or the other output */
 #define ATTN_ERR_LAUNCH (-8)      /* the HIP runtime rejected the kernel launch */
 #define ATTN_ERR_WORKSPACE (-9)   /* workspace smaller than attn_decode_workspace_bytes */
+#define ATTN_ERR_SCRATCH (-10)    /* attn_decode_paged_noalloc: step needs more than
+                                     ATTN_DECODE_SCRATCH_BYTES of scratch */
+
+/* Size of the library's static per-GPU scratch used by attn_decode_paged_noalloc. */
+#define ATTN_DECODE_SCRATCH_BYTES (32ll << 20)
 
 /* flags of attn_fwd_ex */
 #define ATTN_FLAG_HADAMARD_O 1u /* O rows times the normalised Hadamard matrix (FP8 only) */
@@ -295,6 +300,34 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int64_t max_pages_per_seq, int64_t max_seqlen, float softmax_scale,
                       int dtype, float q_descale, float k_descale, float v_descale,
                       void* stream);
+
+/*
+ * attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation, harnesses without an allocator): the same step, the
+ * same kernels and bitwise the same results as attn_decode_paged with a
+ * workspace, but the partial results of the key splits go to a scratch
+ * array the library holds in device memory, ATTN_DECODE_SCRATCH_BYTES
+ * (32 MiB) on each GPU it runs on, kept until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Arguments, checks and status codes are those of attn_decode_paged
+ *   without workspace / workspace_bytes; a step whose
+ *   attn_decode_workspace_bytes(B, H_q, H_kv, max_seqlen, d_v) exceeds
+ *   ATTN_DECODE_SCRATCH_BYTES returns ATTN_ERR_SCRATCH before any HIP call.
+ *   The scratch of the current device is used: `stream` must belong to it.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in
+ * time on one GPU (on different streams, or from different host threads)
+ * race and give undefined results; calls ordered on one stream do not.
+ * The scratch needs no clearing between calls.  ATTN_ERR_LAUNCH is also
+ * returned when the runtime cannot resolve the scratch's device address
+ * (done once per device, on the first call there).
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              float* lse, int64_t B, int64_t H_q, int64_t H_kv, int d_qk, int d_v,
+                              int64_t num_pages, int64_t page_size, int64_t max_pages_per_seq,
+                              int64_t max_seqlen, float softmax_scale, int dtype, float q_descale,
+                              float k_descale, float v_descale, void* stream);
 
 /*
  * attn_decode_workspace_bytes -- workspace attn_decode_paged needs for these

@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
                             "attn_amax_f32", "attn_quantize_fp8",
                             "attn_quantize_e4m3", "attn_hadamard_f32", "attn_hadamard_bf16",
                             "attn_hadamard_amax_f32", "attn_hadamard_quantize_e4m3",
-                            "attn_decode_paged", "attn_decode_workspace_bytes"]), names
+                            "attn_decode_paged", "attn_decode_paged_noalloc",
+                            "attn_decode_workspace_bytes"]), names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert pkg.attn_version() >= 200
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         s = pkg.attn_status_string(code)
         assert s and s != "unknown status"
     assert pkg.attn_status_string(-100) == "unknown status"
@@ -207,6 +208,38 @@ def test_decode_entry_point_rejects(lib):
     assert call(o=K + 64) == -7                   # o inside the key cache
     assert call(workspace=T) == -7                # workspace over the block table
     assert call(lse=O + 16) == -7                 # lse inside o
+
+
+def test_decode_noalloc_rejects_on_the_host(lib):
+    """Host checks of the allocation-free decode: the same argument checks as
+    attn_decode_paged, and steps needing more scratch than the library holds
+    rejected before any HIP call (no GPU needed)."""
+    T, N = 0x70000000, 0x78000000
+
+    def call(**kw):
+        a = dict(q=Q, k_cache=K, v_cache=V, block_table=T, seq_lens=N, o=O, lse=L, B=4, H_q=8,
+                 H_kv=2, d_qk=128, d_v=128, num_pages=64, page_size=64, max_pages_per_seq=16,
+                 max_seqlen=1000, softmax_scale=0.1, dtype=0, q_descale=1.0, k_descale=1.0,
+                 v_descale=1.0)
+        a.update(kw)
+        return pkg.attn_decode_paged_noalloc(*a.values())
+    assert call(q=None) == -1
+    assert call(block_table=None) == -1
+    assert call(B=0) == -2
+    assert call(H_q=48) == -4
+    assert call(d_qk=64) == -4
+    assert call(dtype=3) == -3
+    assert call(softmax_scale=float("nan")) == -5
+    assert call(q=Q + 8) == -6
+    assert call(o=K + 64) == -7
+    assert call(lse=O + 16) == -7
+    # 512 sequences of up to 2^20 keys on 64 query heads: the split partials
+    # need far more than the static scratch
+    big = dict(B=512, H_q=64, H_kv=8, max_seqlen=1 << 20, max_pages_per_seq=1 << 14, num_pages=1 << 20)
+    need = pkg.attn_decode_workspace_bytes(512, 64, 8, 1 << 20, 128)
+    assert need > pkg.ATTN_DECODE_SCRATCH_BYTES
+    assert call(**big) == -10
+    assert "scratch" in pkg.attn_status_string(-10)
 
 
 def test_fwd_ex_flags(lib):
