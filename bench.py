@@ -1,9 +1,15 @@
 """Benchmark: causal prefill attention forward TFLOP/s on one MI355X.
 
 One step = one attn_fwd call over the whole workload (every query block of
-every head), inputs resident in HBM.  Prints ONE JSON line.
+every head), inputs resident in HBM.  Prints ONE JSON line: the headline
+workload (C4 by default) at the top level, and under "also" the same record
+for further workloads (by default C2x, BF16 at 32K, and C5, the FP8 MLA
+shape), each with its own timed steps, roofline, sustained window (power,
+clock, clock-adjusted fraction) and a bitwise determinism check over many
+launches.
 
   python bench.py [--steps K] [--warmup W] [--workload C4] [--gpus 1]
+                  [--also C2x,C5|none] [--det-launches N] [--sub-energy S]
                   [--cpu-seconds 12] [--no-cpu] [--varlen N] [--hadamard]
                   [--energy SECONDS] [--decode D1,D2,D3,D4]
 
@@ -58,6 +64,17 @@ def parse():
     ap.add_argument("--decode", default="",
                     help="also time attn_decode_paged on these decode workloads (comma "
                          "separated names from synth.DECODE_WORKLOADS, or 'all')")
+    ap.add_argument("--also", default="C2x,C5",
+                    help="also measure these workloads in the same run, each as a sub-record "
+                         "of the JSON line with its own timed steps, roofline, sustained "
+                         "window and determinism check ('none' to skip); the metric covers "
+                         "FP8 and BF16 at 32K, and C5 is the pages' MLA shape")
+    ap.add_argument("--sub-energy", type=float, default=3.0,
+                    help="sustained window (seconds) of each sub-record")
+    ap.add_argument("--det-launches", type=int, default=2000,
+                    help="launches of the headline workload whose outputs are each compared "
+                         "bitwise, on the device, with the first launch's (sub-records: a "
+                         "tenth of it)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one float32 elementwise copy of this many MiB before the "
                          "warmup (reads and writes exactly that many bytes): the reference "
@@ -301,6 +318,27 @@ def energy_run(step, flops, torch, seconds):
             pass
 
 
+def determinism(step, o, lse, torch, n):
+    """Run `n` more launches and compare every one's o and lse bitwise with
+    the output before them, on the device (a mismatch counter, read once at
+    the end), so the check does not pace the launches."""
+    if n <= 0:
+        return None
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = o.clone(), lse.clone()
+    bad = torch.zeros((), dtype=torch.int64, device=o.device)
+    for i in range(n):
+        step()
+        bad += ((o.view(torch.int16) != ref_o.view(torch.int16)).any()
+                | (lse.view(torch.int32) != ref_l.view(torch.int32)).any())
+        if i % 64 == 63:
+            torch.cuda.synchronize()  # keep the launch queue short
+    torch.cuda.synchronize()
+    nbad = int(bad.item())
+    return {"launches": n, "identical": nbad == 0, "mismatching_launches": nbad}
+
+
 def time_decode(names, pkg, synth, torch, stream, steps, warmup):
     """HBM throughput of one decode step (attn_decode_paged: the split kernel
     and the merge kernel) per decode workload.  Algorithmic bytes: every
@@ -432,18 +470,12 @@ def time_hadamard(w, host, pkg, torch, stream, attn_ms, dev_in, ds, reps=10):
 
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: the kernel runs on one device and "
-              "multi-GPU runs are not part of this library; use --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    import torch
-
-    import causal_prefill_attention_attn_amd as pkg
-    from causal_prefill_attention_attn_amd import synth
-
-    w = synth.WORKLOADS[args.workload]
+def measure(w, args, torch, pkg, synth, energy_seconds, det_launches, calib_mb=0):
+    """One workload: inputs on the device, warmup, exactly args.steps timed
+    launches (HIP events on the launching stream around each, wall clock
+    around all), a sustained window for power and clock, and the
+    determinism loop.  Returns (record, step, host inputs, device inputs,
+    descales, mean kernel ms)."""
     dtname = "bf16" if w.dtype == synth.BF16 else "fp8"
     log("bench: workload %s (%s)" % (w.name, w.description))
     t, ds, host = device_inputs(w, torch, pkg, synth)
@@ -452,13 +484,13 @@ def main():
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    if args.calib_copy_mb:
-        n = args.calib_copy_mb * (1 << 20) // 4
+    if calib_mb:
+        n = calib_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        log("bench: calibration copy of %d MiB done" % args.calib_copy_mb)
+        log("bench: calibration copy of %d MiB done" % calib_mb)
         del src, dst
 
     def step():
@@ -483,38 +515,27 @@ def main():
     kern_ms = [s.elapsed_time(e) for s, e in ev]
     identical = bool(torch.equal(o.view(torch.int16), ref_o.view(torch.int16)) and
                      torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)))
+    del ref_o, ref_lse
     prof = profiled(w, dtname)
     ms_step = wall * 1e3 / args.steps
     flops = w.causal_flops
     value = flops / (ms_step * 1e-3) / 1e12
     avg_kern = float(np.mean(kern_ms))
     achieved = flops / (avg_kern * 1e-3) / 1e12
-    log("bench: %d steps, wall %.3f ms/step, kernel mean %.3f ms (median %.3f, min %.3f)"
-        % (args.steps, ms_step, avg_kern, float(np.median(kern_ms)), float(np.min(kern_ms))))
-
+    peak = PEAK_TFLOPS[dtname]
+    log("bench: %s %d steps, wall %.3f ms/step, kernel mean %.3f ms (median %.3f, min %.3f)"
+        % (w.name, args.steps, ms_step, avg_kern, float(np.median(kern_ms)), float(np.min(kern_ms))))
     esz = 2 if w.dtype == synth.BF16 else 1
     rows = w.B * w.S * w.H
     compulsory = rows * (2 * w.d_qk + w.d_v) * esz + rows * w.d_v * 2 + w.B * w.H * w.S * 4
-    out = {
-        "metric": "causal prefill attention TFLOP/s (FP8 & BF16) and % of MFMA peak at 32K",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dtname,
-        "data": "synthetic",
-        "config": {"workload": w.name, "description": w.description, "B": w.B, "H": w.H,
-                   "S": w.S, "d_qk": w.d_qk, "d_v": w.d_v, "causal": True,
-                   "softmax_scale": w.softmax_scale, "flops_per_step": flops,
-                   "frac_of_peak": round(value / PEAK_TFLOPS[dtname], 4)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_TFLOPS[dtname], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS[dtname], 4),
+    rec = {
+        "workload": w.name, "description": w.description, "dtype": dtname,
+        "config": {"B": w.B, "H": w.H, "S": w.S, "d_qk": w.d_qk, "d_v": w.d_v, "causal": True,
+                   "softmax_scale": w.softmax_scale, "flops_per_step": flops},
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "TFLOP/s": round(value, 2), "frac_of_peak": round(value / peak, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": prof["traffic"],
                      "kernel": "attn_fwd_%s_kernel<%d>" % (dtname, w.d_qk),
                      "kernel_ms_mean": round(avg_kern, 4),
@@ -523,27 +544,88 @@ def main():
                      "sclk_mhz_profiled": prof["sclk_mhz"],
                      "mfma_busy_profiled": prof["mfma_busy"],
                      "valu_busy_profiled": prof["valu_busy"],
-                     "frac_clock_adjusted": (round(achieved / (PEAK_TFLOPS[dtname] *
-                                                               prof["sclk_mhz"] / 2400.0), 4)
-                                             if prof["sclk_mhz"] else None),
                      "compulsory_bytes": compulsory},
         "bitwise_identical_launches": identical,
+    }
+    if energy_seconds > 0:
+        log("bench: %s sustained run of %.0f s for energy and clock" % (w.name, energy_seconds))
+        en = energy_run(step, flops, torch, energy_seconds)
+        rec["energy"] = en
+        mhz = en.get("gfx_mhz_sampled_median")
+        if mhz and en.get("TFLOP/s"):
+            # throughput and clock of the same sustained window
+            rec["roofline"]["frac_clock_adjusted"] = round(
+                en["TFLOP/s"] / (peak * mhz / 2400.0), 4)
+            rec["roofline"]["frac_clock_adjusted_source"] = (
+                "TFLOP/s of the sustained window over the peak scaled by the gfx clock amdsmi "
+                "sampled in that window (median %.0f MHz)" % mhz)
+    det = determinism(step, o, lse, torch, det_launches)
+    if det is not None:
+        rec["determinism"] = det
+        log("bench: %s %d launches compared bitwise: %s" % (
+            w.name, det["launches"], "identical" if det["identical"] else "MISMATCH"))
+    return rec, step, host, t, ds, avg_kern
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the kernel runs on one device and "
+              "multi-GPU runs are not part of this library; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import causal_prefill_attention_attn_amd as pkg
+    from causal_prefill_attention_attn_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    rec, step, host, t, ds, avg_kern = measure(w, args, torch, pkg, synth, args.energy,
+                                               args.det_launches, args.calib_copy_mb)
+    stream = torch.cuda.current_stream(t[0].device)
+    out = {
+        "metric": "causal prefill attention TFLOP/s (FP8 & BF16) and % of MFMA peak at 32K",
+        "value": rec["TFLOP/s"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": rec["dtype"],
+        "data": "synthetic",
+        "config": dict(workload=w.name, description=w.description, **rec["config"],
+                       frac_of_peak=rec["frac_of_peak"]),
+        "roofline": rec["roofline"],
+        "bitwise_identical_launches": rec["bitwise_identical_launches"],
         "inputs": input_stats(w, host),
     }
+    for k in ("energy", "determinism"):
+        if k in rec:
+            out[k] = rec[k]
     if args.varlen:
         out["varlen"] = time_varlen(w, t, ds, pkg, torch, stream, args.varlen, args.steps)
-    if args.energy > 0:
-        log("bench: sustained run of %.0f s for energy" % args.energy)
-        out["energy"] = energy_run(step, flops, torch, args.energy)
+    if args.hadamard:
+        out["hadamard"] = time_hadamard(w, host, pkg, torch, stream, avg_kern, t, ds)
     if args.decode:
         names = (sorted(synth.DECODE_WORKLOADS) if args.decode == "all"
                  else args.decode.split(","))
         out["decode"] = time_decode(names, pkg, synth, torch, stream, args.steps, args.warmup)
-    if args.hadamard:
-        out["hadamard"] = time_hadamard(w, host, pkg, torch, stream, avg_kern, t, ds)
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, synth)
+    del t, step
+    torch.cuda.empty_cache()
+    also = [] if args.also in ("", "none") else [x for x in args.also.split(",") if x != w.name]
+    if also:
+        out["also"] = {}
+        for name in also:
+            sub, step, _, t, _, _ = measure(synth.WORKLOADS[name], args, torch, pkg, synth,
+                                            args.sub_energy, args.det_launches // 10)
+            out["also"][name] = sub
+            del t, step
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 
