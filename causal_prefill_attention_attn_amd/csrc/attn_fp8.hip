@@ -49,10 +49,13 @@
 //          written directly as the integer round(8*(y + 7) - d): the integer
 //          part of y lands in the exponent field (bias 7) and 8*frac(y) in
 //          the three mantissa bits, i.e. 2^f is replaced by 1 + f.  That is
-//          one multiply-add and one integer conversion per probability
-//          (v_cvt_pk_u8_f32 rounds to nearest even and clamps to [0,255]),
-//          the lean-P technique of "Como o motor de atencao FP8 da Zyphra
-//          funciona" on the miraibroadcast.com page.  The shift d = 0.4567
+//          one multiply-add per probability plus an integer conversion: the
+//          multiply-add yields (256 z + 127.5) / 65535 for the code z, the
+//          16-bit normalised conversion (round to nearest, clamp to [0, 1])
+//          of a pair holds round(z) in each high byte, and one byte permute
+//          gathers four codes, 1.75 instructions per probability (the lean-P
+//          technique of "Como o motor de atencao FP8 da Zyphra funciona" on
+//          the miraibroadcast.com page).  The shift d = 0.4567
 //          makes the approximation unbiased on average (mean of decoded
 //          value / 2^y over a uniform fractional part is 1), so the row sum
 //          and the LSE carry no systematic bias; the block maximum y = 8
@@ -62,8 +65,12 @@
 // issued by waves 0-3 (rows past the end read as zero): eight stages with
 // tile t+4 issued at t and a barrier after every second tile at d = 128,
 // four stages with tile t+3 issued at t and a barrier per tile at d = 192.
+// At d = 128 the bulk of the iterations run eight per pass, one per stage,
+// with every LDS address offset a compile-time constant.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_device.h"
 #include "attn_kernels.h"
@@ -393,6 +400,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       l_run *= alpha;
     }
   };
+  const float c8n = 8.0f * c_log2 * (256.0f / 65535.0f);
   // P = e4m3(2^(c*s - m + k)); k = 8 - ceil(block max - m) puts the block
   // maximum in (2^7, 2^8]; k >= 0 since block max - m <= lazy_log2 <= 8
   auto probs = [&](const f32x16* scur, float bmax, int& pscale) {
@@ -400,17 +408,22 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     pscale = kE8M0One - (int)kf;
     i32x8 pw = __builtin_nondeterministic_value(pw);  // every byte is written below
     if constexpr (kLean) {
-      const float c8 = 8.0f * c_log2;
+      // z = 8 c s + ofs8 is the code in units of 1/8 octave; the 16-bit
+      // normalised conversion of (256 z + 127.5) / 65535 (round to nearest,
+      // clamped to [0, 1]) holds round(z) in its high byte, and one byte
+      // permute gathers the high bytes of two pairs
       const float ofs8 = 8.0f * (7.0f + kf - m_run) - kLeanShift;
+      const float ofsn = (ofs8 * 256.0f + 127.5f) * (1.0f / 65535.0f);
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = w >> 2;
         const int i0 = (w & 3) * 4;
-        unsigned word = (unsigned)pw[w];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(scur[kb][i0 + e], c8, ofs8), e, word);
-        pw[w] = (int)word;
+        const auto lo = __builtin_amdgcn_cvt_pknorm_u16(__builtin_fmaf(scur[kb][i0 + 0], c8n, ofsn),
+                                                        __builtin_fmaf(scur[kb][i0 + 1], c8n, ofsn));
+        const auto hi = __builtin_amdgcn_cvt_pknorm_u16(__builtin_fmaf(scur[kb][i0 + 2], c8n, ofsn),
+                                                        __builtin_fmaf(scur[kb][i0 + 3], c8n, ofsn));
+        pw[w] = (int)__builtin_amdgcn_perm(__builtin_bit_cast(unsigned, hi),
+                                           __builtin_bit_cast(unsigned, lo), 0x07050301u);
       }
     } else {
       const float ofs = kf - m_run;
@@ -556,6 +569,104 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   // unrolled by two so that the two score buffers swap roles without copies;
   // an odd exit copies the scores once
   int t = 0;
+  if constexpr (LY::kPair) {
+    // Steady state: eight iterations per pass, one per LDS stage, so that
+    // every stage index and LDS address offset is a compile-time constant
+    // (no per-tile address or stage arithmetic), and every tile issued ahead
+    // exists (t + 11 < nkt), so no load is tested.  K rows of 128 bytes fill
+    // their 8 chunk slots exactly: no padding loads.
+    static_assert(LY::kKC * 16 == DQK, "unpadded K rows in the steady loop");
+    // per-lane LDS addresses of the K and V^T operand reads in stage 0: K
+    // logical chunk s*4 + part of this lane's row, V^T block d
+    uint32_t kx[4], vx[kDV / 32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      kx[c] = lds_addr(sm.k[0]) + (kbase ^ ((((c >> 1) * 4) + (c & 1)) << 4));
+#pragma unroll
+    for (int d = 0; d < kDV / 32; ++d) vx[d] = lds_addr(sm.v[0]) + (vbase ^ (d << 5));
+    auto issue_c = [&](auto J, int t0) {  // tile t0 + J + 4 into stage (J + 4) % 8
+      constexpr int j = decltype(J)::value;
+      constexpr int buf = (j + 4) % LY::kStages;
+      const uint32_t kb = (uint32_t)((t0 + j + 4) * BN) * rsQK, vb = (uint32_t)((t0 + j + 4) * BN) * rsV;
+      if (wave >= kIssuers) return;
+#pragma unroll
+      for (int i = 0; i < kMine; ++i) {
+        if (i * kIssuers < kKL) buffer_load_lds16(rk, &sm.k[buf][lo_[i]], kb + go[i]);
+        else buffer_load_lds16(rv, &sm.v[buf][lo_[i]], vb + go[i]);
+      }
+    };
+    auto qk_c = [&](auto ST, f32x16* sout) {  // S^T of the tile in stage ST
+      constexpr int st = decltype(ST)::value;
+      sout[0] = f32x16{};
+      sout[1] = f32x16{};
+#pragma unroll
+      for (int s2 = 0; s2 < kSteps; ++s2)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t off = st * LY::kKBytes + kb * 32 * LY::kKPitch;
+          typedef const __attribute__((address_space(3))) i32x4* lds_i32x4;
+          const i32x4 lo = *(lds_i32x4)(uintptr_t)(kx[s2 * 2 + 0] + off);
+          const i32x4 hi = *(lds_i32x4)(uintptr_t)(kx[s2 * 2 + 1] + off);
+          sout[kb] = mfma_f8_plain(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), qreg[s2], sout[kb]);
+        }
+    };
+    auto pv_c = [&](auto ST, const i32x8& pw, int pscale) {
+      constexpr int st = decltype(ST)::value;
+      constexpr int so = st * LY::kVBytes;
+      i32x2 r[2][4];
+      auto vread = [&](int d, i32x2* x) {
+        x[0] = ds_read_tr8<so + 0 * 16 * kDV>(vx[d]);
+        x[1] = ds_read_tr8<so + 1 * 16 * kDV>(vx[d]);
+        x[2] = ds_read_tr8<so + 2 * 16 * kDV>(vx[d]);
+        x[3] = ds_read_tr8<so + 3 * 16 * kDV>(vx[d]);
+      };
+      vread(0, r[0]);
+      vread(1, r[1]);
+#pragma unroll
+      for (int d = 0; d < kDV / 32; ++d) {
+        i32x2* x = r[d & 1];
+        if (d + 1 < kDV / 32) lds_wait4<4>(x[0], x[1], x[2], x[3]);
+        else lds_wait4<0>(x[0], x[1], x[2], x[3]);
+        const i32x8 a = __builtin_shufflevector(
+            __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3),
+            __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[d] = mfma_f8(a, pw, oacc[d], kE8M0One, pscale);
+        if (d + 2 < kDV / 32) vread(d + 2, x);
+      }
+      const f32x4 lt = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lsel, pw, f32x4{}, 0, 0, 0, 0, 0, 0);
+      l_run = __builtin_fmaf(lt[0], __uint_as_float((unsigned)pscale << 23), l_run);
+    };
+    auto step_c = [&](auto J, int t0, f32x16* scur, f32x16* snext, float bcur, float& bnext) {
+      constexpr int j = decltype(J)::value;
+      issue_c(J, t0);
+      __builtin_amdgcn_s_setprio(1);
+      refresh(bcur);
+      int pscale;
+      const i32x8 pw = probs(scur, bcur, pscale);
+      qk_c(std::integral_constant<int, (j + 1) % LY::kStages>{}, snext);
+      __builtin_amdgcn_s_setprio(0);
+      pv_c(std::integral_constant<int, j>{}, pw, pscale);
+      bnext = tile_max(snext);
+#pragma unroll
+      for (int d = 0; d < kDV / 32; ++d) pin(oacc[d]);
+      pin(l_run);
+      pin(bnext);
+      if constexpr (j & 1) {
+        wait_vmcnt<kMine>();
+        barrier_nofence();
+      }
+    };
+    for (; t + 7 < t_fe && t + 11 < nkt; t += 8) {
+      step_c(std::integral_constant<int, 0>{}, t, sa, sb, bmax_a, bmax_b);
+      step_c(std::integral_constant<int, 1>{}, t, sb, sa, bmax_b, bmax_a);
+      step_c(std::integral_constant<int, 2>{}, t, sa, sb, bmax_a, bmax_b);
+      step_c(std::integral_constant<int, 3>{}, t, sb, sa, bmax_b, bmax_a);
+      step_c(std::integral_constant<int, 4>{}, t, sa, sb, bmax_a, bmax_b);
+      step_c(std::integral_constant<int, 5>{}, t, sb, sa, bmax_b, bmax_a);
+      step_c(std::integral_constant<int, 6>{}, t, sa, sb, bmax_a, bmax_b);
+      step_c(std::integral_constant<int, 7>{}, t, sb, sa, bmax_b, bmax_a);
+    }
+  }
   for (; t + 1 < t_fe; t += 2) {
     fast_step(t, sa, sb, bmax_a, bmax_b);
     fast_step(t + 1, sb, sa, bmax_b, bmax_a);
