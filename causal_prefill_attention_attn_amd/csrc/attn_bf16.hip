@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -91,6 +93,15 @@ struct Layout {
   static constexpr int kKBytes = BN * kKPitch;
   static constexpr int kVBytes = BN * kVRow;
 };
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 template <int DQK, int BN>
 struct Smem {
@@ -398,6 +409,97 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // unrolled by two so that the score buffers swap roles without copies; an
   // odd exit copies the scores once
   int t = 0;
+  {
+    // Steady state: four iterations per pass, one per LDS stage, so that
+    // every stage index and LDS address offset is a compile-time constant
+    // (no per-tile address or stage arithmetic), and every tile issued ahead
+    // exists (t + 6 < nkt), so no load is tested.
+    typedef const __attribute__((address_space(3))) uint8_t* lds_u8;
+    const uint32_t kx0 = lds_addr(sm.k[0]);
+    const uint32_t vx0 = lds_addr(sm.v[0]);
+    auto issue_c = [&](auto J, int t0) {  // tile t0 + J + 3 into stage (J + 3) % 4
+      constexpr int j = decltype(J)::value;
+      constexpr int st = (j + kAhead) % kStages;
+      const uint32_t kb0 = (uint32_t)((t0 + j + kAhead) * BN) * rsQK;
+      const uint32_t vb0 = (uint32_t)((t0 + j + kAhead) * BN) * rsV;
+      if (wave >= kIssuers) return;
+#pragma unroll
+      for (int i = 0; i < kMine; ++i) {
+        if (i * kIssuers < kKL)
+          buffer_load_lds16(rk, &sm.k[st][lo_[i]], go[i] == 0xfffffff0u ? go[i] : kb0 + go[i]);
+        else
+          buffer_load_lds16(rv, &sm.v[st][lo_[i]], vb0 + go[i]);
+      }
+    };
+    auto qk_c = [&](auto ST, f32x16* sc) {
+      constexpr int st = decltype(ST)::value;
+#pragma unroll
+      for (int kb = 0; kb < kNKB; ++kb) {
+        sc[kb] = f32x16{};
+#pragma unroll
+        for (int s2 = 0; s2 < kSteps; ++s2) {
+          const bf16x8 kop = __builtin_bit_cast(
+              bf16x8, *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(
+                          kx0 + st * LY::kKBytes + kb * 32 * LY::kKPitch + (kbase ^ (s2 << 5))));
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[s2], sc[kb], 0, 0, 0);
+        }
+      }
+    };
+    auto pv_c = [&](auto ST, const bf16x8* pb) {
+      constexpr int st = decltype(ST)::value;
+      constexpr int kPV = (BN / 16) * (kDV / 32);
+      auto vread = [&](auto M) {
+        constexpr int m = decltype(M)::value;
+        constexpr int u = m / (kDV / 32), d = m % (kDV / 32);
+        constexpr int off = st * LY::kVBytes + u * 16 * kVRow;
+        const uint32_t a = vx0 + (vbase ^ (d << 6));
+        const i16x4 ra = ds_read_tr16<off>(a);
+        const i16x4 rb = ds_read_tr16<off + 8 * kVRow>(a);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(ra, rb, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vop[kPV];
+      vop[0] = vread(std::integral_constant<int, 0>{});
+      vop[1] = vread(std::integral_constant<int, 1>{});
+      auto body = [&](auto M) {
+        constexpr int m = decltype(M)::value;
+        if constexpr (m + 2 < kPV) {
+          vop[m + 2] = vread(std::integral_constant<int, m + 2>{});
+          lds_wait_n<4>(vop[m]);
+        } else if constexpr (m + 1 < kPV) {
+          lds_wait_n<2>(vop[m]);
+        } else {
+          lds_wait_n<0>(vop[m]);
+        }
+        constexpr int u = m / (kDV / 32), d = m % (kDV / 32);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[m], pb[u], oacc[d], 0, 0, 0);
+      };
+      static_for<0, kPV>(body);
+    };
+    auto step_c = [&](auto J, int t0, f32x16* scur, f32x16* snext, float tcur, float& tnext) {
+      constexpr int j = decltype(J)::value;
+      issue_c(J, t0);
+      if constexpr (DQK == 192) __builtin_amdgcn_s_setprio(1);
+      refresh(tcur);
+      bf16x8 pb[BN / 16];
+      probs(scur, pb);
+      qk_c(std::integral_constant<int, (j + 1) % kStages>{}, snext);
+      if constexpr (DQK == 192) __builtin_amdgcn_s_setprio(0);
+      pv_c(std::integral_constant<int, j>{}, pb);
+      tnext = tile_max(snext);
+#pragma unroll
+      for (int d = 0; d < kDV / 32; ++d) pin(oacc[d]);
+      asm volatile("" : "+v"(lacc));
+      pin(tnext);
+      wait_vmcnt<kMine>();
+      barrier_nofence();
+    };
+    for (; t + kStages - 1 < t_fe && t + kStages - 1 + kAhead < nkt; t += kStages) {
+      step_c(std::integral_constant<int, 0>{}, t, sa, sb, tmax_a, tmax_b);
+      step_c(std::integral_constant<int, 1>{}, t, sb, sa, tmax_b, tmax_a);
+      step_c(std::integral_constant<int, 2>{}, t, sa, sb, tmax_a, tmax_b);
+      step_c(std::integral_constant<int, 3>{}, t, sb, sa, tmax_b, tmax_a);
+    }
+  }
   for (; t + 1 < t_fe; t += 2) {
     fast_step(t, sa, sb, tmax_a, tmax_b);
     fast_step(t + 1, sb, sa, tmax_b, tmax_a);

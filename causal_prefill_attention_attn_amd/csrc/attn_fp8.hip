@@ -65,8 +65,8 @@
 // issued by waves 0-3 (rows past the end read as zero): eight stages with
 // tile t+4 issued at t and a barrier after every second tile at d = 128,
 // four stages with tile t+3 issued at t and a barrier per tile at d = 192.
-// At d = 128 the bulk of the iterations run eight per pass, one per stage,
-// with every LDS address offset a compile-time constant.
+// The bulk of the iterations run one per stage per pass (eight at d = 128,
+// four at d = 192), with every LDS address offset a compile-time constant.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -569,30 +569,38 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   // unrolled by two so that the two score buffers swap roles without copies;
   // an odd exit copies the scores once
   int t = 0;
-  if constexpr (LY::kPair) {
-    // Steady state: eight iterations per pass, one per LDS stage, so that
-    // every stage index and LDS address offset is a compile-time constant
-    // (no per-tile address or stage arithmetic), and every tile issued ahead
-    // exists (t + 11 < nkt), so no load is tested.  K rows of 128 bytes fill
-    // their 8 chunk slots exactly: no padding loads.
-    static_assert(LY::kKC * 16 == DQK, "unpadded K rows in the steady loop");
+  {
+    // Steady state: one iteration per LDS stage per pass (eight at d = 128,
+    // four at d = 192), so that every stage index and LDS address offset is
+    // a compile-time constant (no per-tile address or stage arithmetic), and
+    // every tile issued ahead exists, so no load is tested.
+    constexpr int kS = LY::kStages;
+    constexpr int kAhead = LY::kPair ? 4 : 3;     // tiles issued ahead
     // per-lane LDS addresses of the K and V^T operand reads in stage 0: K
     // logical chunk s*4 + part of this lane's row, V^T block d
-    uint32_t kx[4], vx[kDV / 32];
+    uint32_t kx[2 * kSteps], vx[kDV / 32];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 2 * kSteps; ++c)
       kx[c] = lds_addr(sm.k[0]) + (kbase ^ ((((c >> 1) * 4) + (c & 1)) << 4));
 #pragma unroll
     for (int d = 0; d < kDV / 32; ++d) vx[d] = lds_addr(sm.v[0]) + (vbase ^ (d << 5));
-    auto issue_c = [&](auto J, int t0) {  // tile t0 + J + 4 into stage (J + 4) % 8
+    auto issue_c = [&](auto J, int t0) {  // tile t0 + J + kAhead into its stage
       constexpr int j = decltype(J)::value;
-      constexpr int buf = (j + 4) % LY::kStages;
-      const uint32_t kb = (uint32_t)((t0 + j + 4) * BN) * rsQK, vb = (uint32_t)((t0 + j + 4) * BN) * rsV;
+      constexpr int buf = (j + kAhead) % kS;
+      const uint32_t kb = (uint32_t)((t0 + j + kAhead) * BN) * rsQK;
+      const uint32_t vb = (uint32_t)((t0 + j + kAhead) * BN) * rsV;
       if (wave >= kIssuers) return;
 #pragma unroll
       for (int i = 0; i < kMine; ++i) {
-        if (i * kIssuers < kKL) buffer_load_lds16(rk, &sm.k[buf][lo_[i]], kb + go[i]);
-        else buffer_load_lds16(rv, &sm.v[buf][lo_[i]], vb + go[i]);
+        if (i * kIssuers < kKL) {
+          // K rows of 128 bytes fill their chunk slots; at d = 192 the 4
+          // padding slots of a 256-byte row read past the buffer (zeros)
+          const uint32_t g = LY::kKC * 16 == DQK ? kb + go[i]
+                                                 : (go[i] == 0xfffffff0u ? go[i] : kb + go[i]);
+          buffer_load_lds16(rk, &sm.k[buf][lo_[i]], g);
+        } else {
+          buffer_load_lds16(rv, &sm.v[buf][lo_[i]], vb + go[i]);
+        }
       }
     };
     auto qk_c = [&](auto ST, f32x16* sout) {  // S^T of the tile in stage ST
@@ -643,7 +651,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       refresh(bcur);
       int pscale;
       const i32x8 pw = probs(scur, bcur, pscale);
-      qk_c(std::integral_constant<int, (j + 1) % LY::kStages>{}, snext);
+      qk_c(std::integral_constant<int, (j + 1) % kS>{}, snext);
       __builtin_amdgcn_s_setprio(0);
       pv_c(std::integral_constant<int, j>{}, pw, pscale);
       bnext = tile_max(snext);
@@ -651,20 +659,22 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       for (int d = 0; d < kDV / 32; ++d) pin(oacc[d]);
       pin(l_run);
       pin(bnext);
-      if constexpr (j & 1) {
+      if constexpr (!LY::kPair || (j & 1)) {
         wait_vmcnt<kMine>();
         barrier_nofence();
       }
     };
-    for (; t + 7 < t_fe && t + 11 < nkt; t += 8) {
+    for (; t + kS - 1 < t_fe && t + kS - 1 + kAhead < nkt; t += kS) {
       step_c(std::integral_constant<int, 0>{}, t, sa, sb, bmax_a, bmax_b);
       step_c(std::integral_constant<int, 1>{}, t, sb, sa, bmax_b, bmax_a);
       step_c(std::integral_constant<int, 2>{}, t, sa, sb, bmax_a, bmax_b);
       step_c(std::integral_constant<int, 3>{}, t, sb, sa, bmax_b, bmax_a);
-      step_c(std::integral_constant<int, 4>{}, t, sa, sb, bmax_a, bmax_b);
-      step_c(std::integral_constant<int, 5>{}, t, sb, sa, bmax_b, bmax_a);
-      step_c(std::integral_constant<int, 6>{}, t, sa, sb, bmax_a, bmax_b);
-      step_c(std::integral_constant<int, 7>{}, t, sb, sa, bmax_b, bmax_a);
+      if constexpr (kS == 8) {
+        step_c(std::integral_constant<int, 4>{}, t, sa, sb, bmax_a, bmax_b);
+        step_c(std::integral_constant<int, 5>{}, t, sb, sa, bmax_b, bmax_a);
+        step_c(std::integral_constant<int, 6>{}, t, sa, sb, bmax_a, bmax_b);
+        step_c(std::integral_constant<int, 7>{}, t, sb, sa, bmax_b, bmax_a);
+      }
     }
   }
   for (; t + 1 < t_fe; t += 2) {
