@@ -36,11 +36,9 @@
 // The running max m is refreshed when some row of the wave sees a larger
 // tile maximum (rescale skipped otherwise).  With m equal to the row max,
 // the row's largest probability becomes exactly 2^8 before rounding, so the
-// dominant weight of peaked rows is exact in e4m3.  A refresh threshold
-// (lazy_log2 > 0) skips rescales while the new maximum stays within
-// 2^lazy_log2 of m; the per-block exponent absorbs the excess, so results
-// stay correct but the top weight is no longer exact (larger error on
-// peaked rows).
+// dominant weight of peaked rows is exact in e4m3.  (Refreshing only past a
+// threshold saves rescales but makes the top weight inexact: measured a few
+// per cent faster with several times the LSE error of peaked rows.)
 //
 // Two ways to form P (template flag kLean):
 //   exact  p = exp2(c*s - m + k) on the transcendental unit, then
@@ -84,6 +82,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kDV = 128;
 constexpr int kE8M0One = 127;      // E8M0 encoding of 2^0
 constexpr float kLeanShift = 0.4567f;  // lean-P re-centring, in units of 1/8 octave
+// the lean code's offset in the units of the 16-bit normalised conversion:
+// (256 (8 x - kLeanShift) + 127.5) / 65535 = kOfsK x + kOfsC
+constexpr float kOfsK = 2048.0f / 65535.0f;
+constexpr float kOfsC = (127.5f - 256.0f * kLeanShift) / 65535.0f;
 
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int scale_a, int scale_b) {
   // operand formats 0/0 = E4M3 x E4M3; op_sel 0 = byte 0 of each scale VGPR
@@ -216,7 +218,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
                     const uint8_t* __restrict__ v, __bf16* __restrict__ o,
                     float* __restrict__ lse, const int32_t* __restrict__ cu, int64_t total,
                     int S_max, int H, int BH, int nqb, float c_log2,
-                    float v_descale, int causal, float lazy_log2, int rot_o) {
+                    float v_descale, int causal, int rot_o) {
   using LY = Layout<DQK, BN>;
   constexpr int kWaves = 4 * kOcc;
   constexpr int kBM = 32 * kWaves;                 // query rows per workgroup
@@ -389,7 +391,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   };
   // running max refresh; O and l rescaled when some row's max grows
   auto refresh = [&](float bmax) {
-    if (__any(bmax > m_run + lazy_log2)) {
+    if (__any(bmax > m_run)) {
       const float m_new = fmaxf(m_run, bmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -402,18 +404,20 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   };
   const float c8n = 8.0f * c_log2 * (256.0f / 65535.0f);
   // P = e4m3(2^(c*s - m + k)); k = 8 - ceil(block max - m) puts the block
-  // maximum in (2^7, 2^8]; k >= 0 since block max - m <= lazy_log2 <= 8
+  // maximum in (2^7, 2^8]; k >= 0 since block max <= m after the refresh
   auto probs = [&](const f32x16* scur, float bmax, int& pscale) {
-    const float kf = fminf(8.0f - __builtin_ceilf(bmax - m_run), 126.0f);
-    pscale = kE8M0One - (int)kf;
+    // k = 8 - ce with ce = ceil(block max - m) in [-118, 0]: the E8M0 code
+    // of 2^-k is 127 - k = 119 + ce
+    const float ce = fmaxf(__builtin_ceilf(bmax - m_run), -118.0f);
+    pscale = (int)(ce + 119.0f);
     i32x8 pw = __builtin_nondeterministic_value(pw);  // every byte is written below
     if constexpr (kLean) {
-      // z = 8 c s + ofs8 is the code in units of 1/8 octave; the 16-bit
-      // normalised conversion of (256 z + 127.5) / 65535 (round to nearest,
-      // clamped to [0, 1]) holds round(z) in its high byte, and one byte
-      // permute gathers the high bytes of two pairs
-      const float ofs8 = 8.0f * (7.0f + kf - m_run) - kLeanShift;
-      const float ofsn = (ofs8 * 256.0f + 127.5f) * (1.0f / 65535.0f);
+      // z = 8 c s + 8 (7 + k - m) - shift is the code in units of 1/8
+      // octave; the 16-bit normalised conversion of (256 z + 127.5) / 65535
+      // (round to nearest, clamped to [0, 1]) holds round(z) in its high
+      // byte, and one byte permute gathers the high bytes of two pairs.  The
+      // offset is kOfsK (15 - ce - m) + kOfsC in those units.
+      const float ofsn = __builtin_fmaf(-ce, kOfsK, __builtin_fmaf(-m_run, kOfsK, 15.0f * kOfsK + kOfsC));
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = w >> 2;
@@ -426,7 +430,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
                                            __builtin_bit_cast(unsigned, lo), 0x07050301u);
       }
     } else {
-      const float ofs = kf - m_run;
+      const float ofs = (8.0f - ce) - m_run;
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = w >> 2;
@@ -727,15 +731,11 @@ int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float*
   const int BH = B * H;
   const dim3 grid((unsigned)nqb * (unsigned)BH);
   const float c_log2 = softmax_scale * q_descale * k_descale * 1.4426950408889634f;
-  // running-max refresh threshold (log2 units): 0 refreshes on any increase,
-  // which keeps the dominant probability of a peaked row exact; the kernel
-  // also supports up to 8 (fewer rescales, at some cost in accuracy)
-  const float lazy_log2 = 0.0f;
   const bool lean = !exact_p;  // probabilities: lean (default) or exact exp2 + convert
 #define CPATTN_LAUNCH_FP8(DQK, BN, LEAN, OCC)                                                     \
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, BN, LEAN, OCC>), grid, dim3(256 * OCC), 0, stream, \
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, cu, \
-                     total, S, H, BH, nqb, c_log2, v_descale, causal, lazy_log2, (int)rot_o)
+                     total, S, H, BH, nqb, c_log2, v_descale, causal, (int)rot_o)
   if (d_qk == 128) {
     if (lean) CPATTN_LAUNCH_FP8(128, 64, true, 2);
     else CPATTN_LAUNCH_FP8(128, 64, false, 2);
