@@ -330,7 +330,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   a.q_descale = q_descale;
   a.k_descale = k_descale;
   a.v_descale = v_descale;
-  cpattn::decode_split_policy(B, H_kv, max_seqlen, &a.split, &a.nsplit);
+  cpattn::decode_launch_policy(a, &a.split, &a.nsplit);
   rc = cpattn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
   return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

@@ -65,6 +65,9 @@ struct DecodeArgs {
   int split, nsplit;
 };
 void decode_split_policy(int64_t B, int64_t Hkv, int64_t max_seqlen, int* split, int* nsplit);
+// The split a call uses: decode_split_policy for e4m3, longer splits for bf16
+// (never more of them).
+void decode_launch_policy(const DecodeArgs& a, int* split, int* nsplit);
 int64_t decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seqlen);
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
 

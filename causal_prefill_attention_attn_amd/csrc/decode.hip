@@ -25,7 +25,9 @@
 //
 // Inside a workgroup: 4 waves; a wave takes tiles of 16 consecutive keys
 // (tiles w, w+4, ...), which lie in one page since pages hold a multiple of
-// 16 keys and splits start at multiples of 64.  The scores of a tile for the
+// 16 keys and splits start at multiples of 64.  Tiles reach the wave through
+// a ring of LDS slots filled by buffer-to-LDS loads (decode_split_kernel
+// below says why).  The scores of a tile for the
 // G query heads of the key/value head are one 16x16 matrix-core product
 // (keys x heads, heads past G are zero columns).  In its accumulator, lane
 // group j (16 lanes) holds keys 4j .. 4j+3 of the tile and lane j*16 + g
@@ -40,6 +42,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "attn_device.h"
 #include "attn_kernels.h"
@@ -67,30 +70,6 @@ struct RowPart {
   uint32_t a[kA];
   uint32_t b[kB > 0 ? kB : 1];
 };
-
-template <int DQK, bool kFP8>
-__device__ __forceinline__ RowPart<DQK, kFP8> load_row(const uint8_t* row, int sub) {
-  constexpr int esz = kFP8 ? 1 : 2;
-  RowPart<DQK, kFP8> r;
-  if constexpr (kFP8) {
-    const u32x2 x = *reinterpret_cast<const u32x2*>(row + sub * 8);
-    r.a[0] = x[0];
-    r.a[1] = x[1];
-    if constexpr (DQK == 192) r.b[0] = *reinterpret_cast<const uint32_t*>(row + 128 + sub * 4);
-  } else {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(row + sub * 16);
-    r.a[0] = x[0];
-    r.a[1] = x[1];
-    r.a[2] = x[2];
-    r.a[3] = x[3];
-    if constexpr (DQK == 192) {
-      const u32x2 y = *reinterpret_cast<const u32x2*>(row + 128 * esz + sub * 8);
-      r.b[0] = y[0];
-      r.b[1] = y[1];
-    }
-  }
-  return r;
-}
 
 // Words -> fp32 values, in element order.
 __device__ __forceinline__ void bf16_words(const uint32_t* w, int n, float* out) {
@@ -190,74 +169,169 @@ __device__ __forceinline__ void row_values(const RowPart<DQK, kFP8>& r, float* o
   }
 }
 
-// Tiles each wave keeps in flight beyond the one it works on: chosen so that
-// the ring of tile buffers (16 registers per e4m3 tile, 32 per bf16 tile)
-// leaves the kernel's occupancy where it was with one tile ahead.
-template <bool kFP8, int G>
-constexpr int prefetch_tiles() {
-  if (kFP8) return G <= 4 ? 3 : 1;
-  return G <= 2 ? 2 : 1;
+// How the cache reaches the arithmetic.  Each wave streams its 16-key tiles
+// into a private ring of slots in LDS with buffer-to-LDS loads (16 bytes per
+// lane, 1 KB per instruction), waits for the oldest with an explicit vmcnt
+// count and reads it back with LDS reads where it is used.  No loaded data is
+// held in registers across the loop: with a ring of tiles in registers the
+// compiler's wait count at the loop head falls back to waiting for every
+// load in flight, once per ring, and the prefetch drains.  Here every wait is
+// exact, and no registers are spent on tiles in flight.
+template <int DQK, bool kFP8>
+struct LdsTile {
+  static constexpr int kEsz = kFP8 ? 1 : 2;
+  static constexpr int kRowK = DQK * kEsz;  // bytes of a key row of one head
+  static constexpr int kPitchK = (kRowK + 127) / 128 * 128;  // whole 128-byte swizzle groups
+  static constexpr int kRowV = kDV * kEsz;
+  static constexpr int kKBytes = kTile * kPitchK;
+  static constexpr int kVBytes = kTile * kRowV;
+  static constexpr int kBytes = kKBytes + kVBytes;
+  static constexpr int kLoadsK = kKBytes / 1024;  // 1 KB loads per tile
+  static constexpr int kLoadsV = kVBytes / 1024;
+  static constexpr int kLoads = kLoadsK + kLoadsV;
+  // slots: at most 72 KB of ring per workgroup, so that two workgroups fit
+  // in a CU's LDS; between 2 and 4
+  static constexpr int kFit = 73728 / (kWaves * kBytes);
+  static constexpr int kDeep = kFit < 2 ? 2 : (kFit > 4 ? 4 : kFit);
+};
+// With grouped query heads (G > 1) a tile costs a wave several times the
+// vector work of G = 1, and more resident workgroups (two slots: four per
+// CU) hide it better than a deeper ring; with one head per key/value head
+// the deeper ring streams best.
+template <int DQK, int G, bool kFP8>
+constexpr int decode_ring() {
+  return G > 1 ? 2 : LdsTile<DQK, kFP8>::kDeep;
+}
+
+// 16-byte chunk c of key row `row` sits at chunk kswz(c, row) of its LDS
+// row: the low three bits are XORed with the row, so the 16 rows that one
+// quarter read touches spread over the banks.  The map is its own inverse.
+__device__ __forceinline__ int kswz(int c, int row) { return (c & ~7) | ((c ^ row) & 7); }
+
+template <int N>
+__device__ __forceinline__ void decode_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// value row part from LDS, as inline assembly so that the wait-count pass
+// does not make it wait for the buffer-to-LDS loads in flight; the result is
+// ordered with decode_lds_wait before use
+template <bool kFP8>
+struct VRead {
+  typedef typename std::conditional<kFP8, i32x2, i32x4>::type T;
+};
+template <bool kFP8, int OFF>
+__device__ __forceinline__ typename VRead<kFP8>::T v_read(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  typename VRead<kFP8>::T r;
+  if constexpr (kFP8)
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  else
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+__device__ __forceinline__ u32x4 k_read(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+// s_waitcnt lgkmcnt(0) tied to the value reads, then to every key chunk:
+// nothing that reads these registers can be placed above the wait
+template <typename T, int N>
+__device__ __forceinline__ void decode_lds_wait(T& a, T& b, T& c, T& d, u32x4 (&k)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(k[i]));
 }
 
 template <int DQK, int G, bool kFP8>
 __global__ void __launch_bounds__(64 * kWaves)
 decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
-                    const uint8_t* __restrict__ vc, const int32_t* __restrict__ table,
-                    const int32_t* __restrict__ lens, float* __restrict__ opart,
-                    float* __restrict__ lpart, int Hkv, int maxp, int npages, int ps_log2,
-                    int lcap, int split, int nsplit, float c_log2, float v_descale) {
-  constexpr int esz = kFP8 ? 1 : 2;
+                        const uint8_t* __restrict__ vc, const int32_t* __restrict__ table,
+                        const int32_t* __restrict__ lens, float* __restrict__ opart,
+                        float* __restrict__ lpart, int Hkv, int maxp, int npages, int ps_log2,
+                        int lcap, int split, int nsplit, float c_log2, float v_descale) {
+  using LT = LdsTile<DQK, kFP8>;
+  using QT = Quarter<DQK, kFP8>;
+  constexpr int esz = LT::kEsz;
+  constexpr int kRing = decode_ring<DQK, G, kFP8>();
+  constexpr int kQC = QT::kWords / 4;  // 16-byte chunks in a quarter row
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kWaves][kRing][LT::kBytes];
+  __shared__ f32x4 sP[kWaves][64];
+  __shared__ float sA[kWaves][64];
+  __shared__ float sM[kWaves][G], sL[kWaves][G];
+  static_assert(sizeof(float) * kWaves * G * kDV <= sizeof(ring), "merge buffer overlays the ring");
+
   const int sp = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  int L = lens[b];
-  L = L < 0 ? 0 : (L > lcap ? lcap : L);
-  const int k0 = sp * split;
-  if (k0 >= L) return;  // whole workgroup: this split is past the sequence's end
-  const int k1 = min(L, k0 + split);
-  const int ntile = (k1 - k0 + kTile - 1) / kTile;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4, sub = lane & 15;
   const int Hq = Hkv * G;
   const int ps = 1 << ps_log2;
+  const int k0 = sp * split;
 
+  // The sequence length, this split's pages and the query are loaded
+  // together: neither the pages nor the query depend on the length, so the
+  // first tile loads wait one memory round trip, not two.  Pages: one per
+  // lane (a split of at most 1024 keys spans at most 64 pages of at least 16
+  // keys); tile t takes its page by readlane.
+  const int p0 = k0 >> ps_log2;
+  const int npmax = ((k0 + split - 1) >> ps_log2) - p0 + 1;
+  const int32_t* trow = table + (int64_t)b * maxp;
+  int pg = 0;
+  if (lane < npmax && p0 + lane < maxp) pg = trow[p0 + lane];
   // B operand: column sub is query head hk*G + sub, a zero column for sub >= G
-  using QT = Quarter<DQK, kFP8>;
   QT qq = load_quarter<DQK, kFP8>(q + ((int64_t)b * Hq + hk * G + (sub < G ? sub : 0)) * DQK * esz,
                                   grp);
-  if (sub >= G) {
-#pragma unroll
-    for (int i = 0; i < QT::kWords; ++i) qq.w[i] = 0u;
-  }
+  int L = lens[b];
+  L = L < 0 ? 0 : (L > lcap ? lcap : L);
+  if (k0 >= L) return;  // whole workgroup: this split is past the sequence's end
+  const int k1 = min(L, k0 + split);
+  const int ntile = (k1 - k0 + kTile - 1) / kTile;
+  pg = pg < 0 ? 0 : (pg >= npages ? npages - 1 : pg);
 
   const int64_t rsK = (int64_t)Hkv * DQK * esz;  // bytes between slots
   const int64_t rsV = (int64_t)Hkv * kDV * esz;
   const uint8_t* kbase = kc + (int64_t)hk * DQK * esz;
   const uint8_t* vbase = vc + (int64_t)hk * kDV * esz;
-  const int32_t* trow = table + (int64_t)b * maxp;
 
-  struct Tile {
-    QT k;                      // key row sub of the tile, quarter grp
-    RowPart<128, kFP8> v[4];   // value rows 4*grp + r, columns 8*sub .. 8*sub+7
-  };
-  // keys at or past k1 read the tile's first row (a valid key) and are
-  // masked below
-  auto load_tile = [&](int t) {
-    Tile x;
+  // Tile t of the split (keys k0 + 16t ..) into ring slot `slot`.  Lane l's
+  // 16 bytes of load j land at byte 1024 j + 16 l of the slot: K rows of
+  // kPitchK bytes (chunks swizzled; padding chunks of d = 192 rows read past
+  // the buffer, i.e. zeros), then V rows.  Keys at or past k1 read the
+  // tile's first row (a valid key); they are masked in the scores.  A tile
+  // of 16 keys lies in one page (pages hold a power of two >= 16 keys, tiles
+  // start at multiples of 16); its buffer resource starts at the tile's
+  // first slot, so offsets stay small for any cache size.
+  auto issue = [&](int t, int slot) {
     const int key0 = k0 + t * kTile;
-    int page = trow[key0 >> ps_log2];
-    page = page < 0 ? 0 : (page >= npages ? npages - 1 : page);
+    const int page = __builtin_amdgcn_readlane(pg, (key0 >> ps_log2) - p0);
     const int64_t slot0 = (int64_t)page * ps + (key0 & (ps - 1));
-    x.k = load_quarter<DQK, kFP8>(kbase + (slot0 + (key0 + sub < k1 ? sub : 0)) * rsK, grp);
+    const int nvalid = k1 - key0;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + slot0 * rsK, (uint32_t)(kTile * rsK));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + slot0 * rsV, (uint32_t)(kTile * rsV));
+    uint8_t* dst = ring[wave][slot];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int dk = 4 * grp + r;
-      x.v[r] = load_row<128, kFP8>(vbase + (slot0 + (key0 + dk < k1 ? dk : 0)) * rsV, sub);
+    for (int j = 0; j < LT::kLoadsK; ++j) {
+      const int pos = j * 1024 + 16 * lane;
+      const int row = pos / LT::kPitchK;
+      const int c = kswz((pos % LT::kPitchK) / 16, row);
+      const uint32_t off = c * 16 >= LT::kRowK
+                               ? 0xFFFFFFF0u
+                               : (uint32_t)((row < nvalid ? row : 0) * rsK + c * 16);
+      buffer_load_lds16(rk, dst + j * 1024, off);
     }
-    return x;
+#pragma unroll
+    for (int j = 0; j < LT::kLoadsV; ++j) {
+      const int pos = j * 1024 + 16 * lane;
+      const int row = pos / LT::kRowV;
+      const uint32_t off = (uint32_t)((row < nvalid ? row : 0) * rsV + pos % LT::kRowV);
+      buffer_load_lds16(rv, dst + LT::kKBytes + j * 1024, off);
+    }
   };
 
-  // softmax stream of (lane group grp, head sub): keys 4*grp .. 4*grp+3 of
-  // every tile, in log2 units (meaningful for sub < G)
   float m_s = kNoKeys, l_s = 0.0f;
   float o[G][8];
 #pragma unroll
@@ -265,16 +339,27 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[g][e] = 0.0f;
 
-  // wave-private exchange slots: lane l's four probabilities and its rescale
-  // factor.  Only this wave touches them, and a wave's LDS accesses complete
-  // in order, so no workgroup barrier is needed.
-  __shared__ f32x4 sP[kWaves][64];
-  __shared__ float sA[kWaves][64];
-
-  // one tile: scores, online softmax update, P.V
-  auto process = [&](const Tile& x, int t) {
+  // one tile from ring slot `slot`: scores, online softmax update, P.V
+  auto process = [&](int slot, int t) {
     const int key0 = k0 + t * kTile;
-    const f32x4 acc = tile_scores<DQK, kFP8>(x.k, qq);
+    const uint32_t base = lds_addr(ring[wave][slot]);
+    // key row sub, quarter grp; value rows 4*grp + r, columns 8*sub .. +7
+    u32x4 kx[kQC];
+#pragma unroll
+    for (int i = 0; i < kQC; ++i)
+      kx[i] = k_read(base + sub * LT::kPitchK + kswz(grp * kQC + i, sub) * 16);
+    const uint32_t va = base + LT::kKBytes + grp * 4 * LT::kRowV + sub * 8 * esz;
+    auto v0 = v_read<kFP8, 0>(va);
+    auto v1 = v_read<kFP8, LT::kRowV>(va);
+    auto v2 = v_read<kFP8, 2 * LT::kRowV>(va);
+    auto v3 = v_read<kFP8, 3 * LT::kRowV>(va);
+    decode_lds_wait(v0, v1, v2, v3, kx);
+    QT kq;
+#pragma unroll
+    for (int i = 0; i < kQC; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kq.w[4 * i + c] = kx[i][c];
+    const f32x4 acc = tile_scores<DQK, kFP8>(kq, qq);
     f32x4 p;
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = key0 + 4 * grp + i < k1 ? acc[i] * c_log2 : -INFINITY;
@@ -288,11 +373,11 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     sP[wave][lane] = p;
     sA[wave][lane] = alpha;
     __builtin_amdgcn_wave_barrier();
-    f32x4 pg[G];
+    f32x4 pg4[G];
     float al[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      pg[g] = sP[wave][16 * grp + g];
+      pg4[g] = sP[wave][16 * grp + g];
       al[g] = sA[wave][16 * grp + g];
     }
     __builtin_amdgcn_wave_barrier();
@@ -300,39 +385,56 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[g][e] *= al[g];
+    RowPart<128, kFP8> vr[4];
+    auto put = [&](RowPart<128, kFP8>& r, const typename VRead<kFP8>::T& x) {
+#pragma unroll
+      for (int i = 0; i < RowPart<128, kFP8>::kA; ++i) r.a[i] = (uint32_t)x[i];
+    };
+    put(vr[0], v0);
+    put(vr[1], v1);
+    put(vr[2], v2);
+    put(vr[3], v3);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float vv[8];
-      row_values<128, kFP8>(x.v[r], vv);
+      row_values<128, kFP8>(vr[r], vv);
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] = fmaf(pg[g][r], vv[e], o[g][e]);
+        for (int e = 0; e < 8; ++e) o[g][e] = fmaf(pg4[g][r], vv[e], o[g][e]);
     }
   };
 
-  // Ring of kAhead + 1 tile buffers in registers, indexed at compile time
-  // (the loop is unrolled by the ring size): while tile t is processed,
-  // tiles t+4 .. t+4*kAhead are in flight.  The body has no condition, so the
-  // compiler's count of outstanding loads stays exact: the wave's tile count
-  // is rounded up to whole rings, loads past the last tile reload it (a cache
-  // hit) and tiles past the last one are processed fully masked, which
-  // leaves m, l and o unchanged (alpha = 1, p = 0).
-  constexpr int kAhead = prefetch_tiles<kFP8, G>();
-  constexpr int kRing = kAhead + 1;
+  // wave w takes tiles w, w+4, ...; its i-th tile goes to slot i % kRing.
+  // Before tile i is read, the loads of tiles i+1 .. i+kRing-1 may still be
+  // in flight: kLoads each.  The slot that tile i + kRing - 1 refills was
+  // read (its reads waited on) in the previous step.
   const int nmine = wave < ntile ? (ntile - wave + kWaves - 1) / kWaves : 0;
-  Tile ring[kRing];
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) ring[i] = load_tile(min(wave + kWaves * i, ntile - 1));
-  for (int it = 0; it < nmine; it += kRing) {
+  for (int i = 0; i < kRing - 1; ++i)
+    if (i < nmine) issue(wave + kWaves * i, i);
+  // zero columns past G, after the first tile loads are issued (using the
+  // query earlier would make them wait for it)
+  if (sub >= G) {
+#pragma unroll
+    for (int i = 0; i < QT::kWords; ++i) qq.w[i] = 0u;
+  }
+  for (int i0 = 0; i0 < nmine; i0 += kRing) {
 #pragma unroll
     for (int j = 0; j < kRing; ++j) {
-      const int t = wave + kWaves * (it + j);
-      ring[(j + kAhead) % kRing] = load_tile(min(t + kWaves * kAhead, ntile - 1));
-      process(ring[j], t);
-      // keep each step's loads in its own step: hoisting later loads only
-      // lengthens register live ranges
-      __builtin_amdgcn_sched_barrier(0);
+      const int i = i0 + j;
+      if (i >= nmine) break;
+      const int t = wave + kWaves * i;
+      if (i + kRing - 1 < nmine) {
+        issue(t + kWaves * (kRing - 1), (j + kRing - 1) % kRing);
+        decode_wait_vmcnt<LT::kLoads * (kRing - 1)>();
+      } else {
+        const int younger = nmine - 1 - i;  // 0 .. kRing-2
+        if (younger == 0) decode_wait_vmcnt<0>();
+        else if (younger == 1) decode_wait_vmcnt<LT::kLoads>();
+        else decode_wait_vmcnt<2 * LT::kLoads>();
+      }
+      process(j, t);
     }
   }
 
@@ -369,9 +471,10 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     m[g] = M;
   }
 
-  // merge the waves through LDS, in wave order
-  __shared__ float sO[kWaves][G][kDV];
-  __shared__ float sM[kWaves][G], sL[kWaves][G];
+  // merge the waves through LDS, in wave order; the partial outputs overlay
+  // the ring, which every wave has finished reading at the barrier
+  __syncthreads();
+  float (*sO)[G][kDV] = reinterpret_cast<float (*)[G][kDV]>(&ring[0][0][0]);
   if (grp == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -423,6 +526,31 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
     if (lse != nullptr && d == 0) lse[bh] = -INFINITY;
     return;
   }
+  // up to 32 splits: every partial is loaded at once (one memory round
+  // trip), then combined in split order as below
+  if (ns <= 32) {
+    float lv[32], ov[32];
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      lv[s] = s < ns ? lp[s] : -INFINITY;
+      ov[s] = s < ns ? op[(int64_t)s * kDV + d] : 0.0f;
+    }
+    float M = lv[0];
+#pragma unroll
+    for (int s = 1; s < 32; ++s) M = fmaxf(M, lv[s]);
+    float wsum = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      if (s < ns) {
+        const float w = expf(lv[s] - M);
+        wsum += w;
+        acc = fmaf(w, ov[s], acc);
+      }
+    }
+    o[(int64_t)bh * kDV + d] = (__bf16)(acc / wsum);
+    if (lse != nullptr && d == 0) lse[bh] = M + logf(wsum);
+    return;
+  }
   // unrolled so that the loads of several splits are in flight together;
   // the sums still run in split order
   float M = lp[0];
@@ -465,19 +593,43 @@ void launch_split_g(const DecodeArgs& a, int G, float* opart, float* lpart, floa
 
 }  // namespace
 
-void decode_split_policy(int64_t B, int64_t Hkv, int64_t max_seqlen, int* split, int* nsplit) {
-  // about 4096 workgroups (16 per CU) if every sequence had max_seqlen keys;
-  // splits of 256 .. 1024 keys, a multiple of 64.  The cap keeps shorter
-  // sequences of a ragged batch spread over several workgroups (workgroups
-  // past a sequence's end return at once).
+namespace {
+// Keys per split: about `target` workgroups if every sequence had max_seqlen
+// keys, a multiple of 64 in [256, cap].  Sequences shorter than max_seqlen
+// leave workgroups that return at once.
+int split_keys(int64_t B, int64_t Hkv, int64_t max_seqlen, int64_t target, int64_t cap) {
   const int64_t per = B * Hkv;
-  const int64_t want = (4096 + per - 1) / per;
+  const int64_t want = (target + per - 1) / per;
   int64_t sp = (max_seqlen + want - 1) / want;
   sp = (sp + 63) / 64 * 64;
   if (sp < 256) sp = 256;
-  if (sp > 1024) sp = 1024;
-  *split = (int)sp;
+  if (sp > cap) sp = cap;
+  return (int)sp;
+}
+}  // namespace
+
+void decode_split_policy(int64_t B, int64_t Hkv, int64_t max_seqlen, int* split, int* nsplit) {
+  // about 4096 workgroups (16 per CU), splits of at most 1024 keys: the e4m3
+  // kernels' policy, and the most splits any call uses (sizes the workspace)
+  const int sp = split_keys(B, Hkv, max_seqlen, 4096, 1024);
+  *split = sp;
   *nsplit = (int)((max_seqlen + sp - 1) / sp);
+}
+
+void decode_launch_policy(const DecodeArgs& a, int* split, int* nsplit) {
+  decode_split_policy(a.B, a.Hkv, a.max_seqlen, split, nsplit);
+  if (a.dtype_fp8) return;
+  // bf16 rows carry half the vector work per byte of e4m3 ones: fewer,
+  // longer splits (about 512 workgroups, up to 4096 keys) stream better.  A
+  // split spans at most 64 pages (one page index per lane).  Never more
+  // splits than the workspace holds.
+  const int sp = split_keys(a.B, a.Hkv, a.max_seqlen, 512,
+                            a.page_size * 64 < 4096 ? a.page_size * 64 : 4096);
+  const int ns = (int)((a.max_seqlen + sp - 1) / sp);
+  if (ns <= *nsplit) {
+    *split = sp;
+    *nsplit = ns;
+  }
 }
 
 int64_t decode_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t max_seqlen) {
