@@ -156,9 +156,12 @@ def input_stats(w, host, nrows=64):
             "n_eff_median": round(float(np.median(neff)), 2)}
 
 
-def cpu_baseline(w, host, seconds, synth):
+def cpu_baseline(w, host, seconds, synth, gpu_head0=None):
     """Time the fp64 oracle on a bounded sample of the same workload: a growing
-    set of query rows of head 0, until about `seconds` of CPU work."""
+    set of query rows of head 0, until about `seconds` of CPU work.  With
+    `gpu_head0` ({name: (o [B,S,d_v], lse [B,S])} of head 0 from GPU launches)
+    the same oracle rows also give the accuracy of each GPU output: pooled
+    relative L2 of O, the worst row's relative L2 and the largest |dlse|."""
     import oracle
     oracle.build()
     qf, kf, vf = host
@@ -172,22 +175,43 @@ def cpu_baseline(w, host, seconds, synth):
                for x, d in zip((qf, kf, vf), ds)]
     rng = np.random.default_rng(4242)
     n, spent, flops, nrows = 8, 0.0, 0.0, 0
+    got = []  # (rows, o [B,rows,d_v], lse [B,rows]) of every chunk
     full_flops = w.B * w.H * w.S * (w.S + 1) / 2.0 * (w.d_qk + w.d_v) * 2.0
     while spent < seconds:
         # each chunk draws distinct rows; chunks are capped at S rows and repeat
         # until the time budget is spent
         rows = np.sort(rng.choice(w.S, size=min(n, w.S), replace=False)).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.attention(enc[0], enc[1], enc[2], w.dtype, w.softmax_scale, True, rows=rows,
-                         q_descale=ds[0], k_descale=ds[1], v_descale=ds[2])
+        ro, rl = oracle.attention(enc[0], enc[1], enc[2], w.dtype, w.softmax_scale, True,
+                                  rows=rows, q_descale=ds[0], k_descale=ds[1], v_descale=ds[2])
         spent += time.perf_counter() - t0
+        got.append((rows, ro[:, :, 0, :], rl[:, 0, :]))
         flops += float(np.sum(rows + 1)) * (w.d_qk + w.d_v) * 2.0 * w.B
         nrows += rows.size
         n *= 2
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "full_run_estimate_s": round(spent * full_flops / flops, 1),
-            "sample": "%d uniformly drawn query rows (chunks of at most S distinct rows) of head 0 (batch %d) of %s, causal, "
-                      "fp64 oracle, %.1f s" % (nrows, w.B, w.name, spent)}
+    res = {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "kind": "oracle", "full_run_estimate_s": round(spent * full_flops / flops, 1),
+           "sample": "%d uniformly drawn query rows (chunks of at most S distinct rows) of head 0 (batch %d) of %s, causal, "
+                     "fp64 oracle, %.1f s" % (nrows, w.B, w.name, spent)}
+    if gpu_head0:
+        rows = np.concatenate([g[0] for g in got])
+        ro = np.concatenate([g[1] for g in got], axis=1)   # [B, n, d_v]
+        rl = np.concatenate([g[2] for g in got], axis=1)   # [B, n]
+        rows, first = np.unique(rows, return_index=True)  # chunks may repeat rows
+        ro, rl = ro[:, first], rl[:, first]
+        acc = {"distinct_rows": int(rows.size) * w.B, "head": 0}
+        for name, (go, gl) in gpu_head0.items():
+            d = go[:, rows, :].astype(np.float64) - ro
+            num = np.linalg.norm(d, axis=-1)
+            den = np.linalg.norm(ro, axis=-1)
+            live = den > 0
+            acc[name] = {
+                "o_rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ro)),
+                "o_worst_row_rel_l2": float((num[live] / den[live]).max()),
+                "o_row_rel_l2_rms": float(np.sqrt(np.mean((num[live] / den[live]) ** 2))),
+                "lse_max_abs_diff": float(np.abs(gl[:, rows].astype(np.float64) - rl).max())}
+        res["gpu_vs_oracle"] = acc
+    return res
 
 
 def time_varlen(w, t, ds, pkg, torch, stream, nseq, reps):
@@ -516,6 +540,18 @@ def measure(w, args, torch, pkg, synth, energy_seconds, det_launches, calib_mb=0
     identical = bool(torch.equal(o.view(torch.int16), ref_o.view(torch.int16)) and
                      torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)))
     del ref_o, ref_lse
+    # head 0 of the outputs, for the accuracy figures of the oracle leg; for
+    # e4m3 also one (untimed) launch with exact-rounded probabilities
+    head0 = {("lean_p" if dtname == "fp8" else "default"):
+             (o[:, :, 0].float().cpu().numpy(), lse[:, 0].cpu().numpy())}
+    if dtname == "fp8":
+        oe, le = torch.empty_like(o), torch.empty_like(lse)
+        pkg.flash_attn_func(t[0], t[1], t[2], softmax_scale=w.softmax_scale, causal=True,
+                            q_descale=ds[0], k_descale=ds[1], v_descale=ds[2], exact_p=True,
+                            out=oe, lse=le)
+        torch.cuda.synchronize()
+        head0["exact_p"] = (oe[:, :, 0].float().cpu().numpy(), le[:, 0].cpu().numpy())
+        del oe, le
     prof = profiled(w, dtname)
     ms_step = wall * 1e3 / args.steps
     flops = w.causal_flops
@@ -564,7 +600,7 @@ def measure(w, args, torch, pkg, synth, energy_seconds, det_launches, calib_mb=0
         rec["determinism"] = det
         log("bench: %s %d launches compared bitwise: %s" % (
             w.name, det["launches"], "identical" if det["identical"] else "MISMATCH"))
-    return rec, step, host, t, ds, avg_kern
+    return rec, step, host, t, ds, avg_kern, head0
 
 
 def main():
@@ -579,8 +615,8 @@ def main():
     from causal_prefill_attention_attn_amd import synth
 
     w = synth.WORKLOADS[args.workload]
-    rec, step, host, t, ds, avg_kern = measure(w, args, torch, pkg, synth, args.energy,
-                                               args.det_launches, args.calib_copy_mb)
+    rec, step, host, t, ds, avg_kern, head0 = measure(w, args, torch, pkg, synth, args.energy,
+                                                      args.det_launches, args.calib_copy_mb)
     stream = torch.cuda.current_stream(t[0].device)
     out = {
         "metric": "causal prefill attention TFLOP/s (FP8 & BF16) and % of MFMA peak at 32K",
@@ -614,15 +650,15 @@ def main():
         out["decode"] = time_decode(names, pkg, synth, torch, stream, args.steps, args.warmup)
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, synth)
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds, synth, head0)
     del t, step
     torch.cuda.empty_cache()
     also = [] if args.also in ("", "none") else [x for x in args.also.split(",") if x != w.name]
     if also:
         out["also"] = {}
         for name in also:
-            sub, step, _, t, _, _ = measure(synth.WORKLOADS[name], args, torch, pkg, synth,
-                                            args.sub_energy, args.det_launches // 10)
+            sub, step, _, t, _, _, _ = measure(synth.WORKLOADS[name], args, torch, pkg, synth,
+                                               args.sub_energy, args.det_launches // 10)
             out["also"][name] = sub
             del t, step
             torch.cuda.empty_cache()
