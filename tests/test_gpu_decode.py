@@ -136,3 +136,42 @@ def test_decode_out_of_range_pages_are_clamped(oracle):
     ro, rl = oracle.decode_paged(*host, np.asarray(lens), synth.BF16, 1.0 / math.sqrt(128))
     err = np.linalg.norm(go[0] - ro[0]) / np.linalg.norm(ro[0])
     assert err <= ROW_TOL, err
+
+
+@pytest.mark.parametrize("ps", [64, 16])
+def test_decode_bf16_long_splits(oracle, ps):
+    """bf16 caches take fewer, longer key splits (at most 4096 keys and 64
+    pages): 16 sequences of up to 4096 keys on 16 key/value heads give splits
+    of 2048 keys, i.e. 32 pages of 64 keys, or with pages of 16 keys the
+    64-page cap of 1024 keys."""
+    lens = [4096] * 15 + [3000]
+    host, ds, dev = _inputs(oracle, synth.BF16, lens, 32, 16, 128, ps, 77 + ps)
+    print("decode bf16 long splits, page %d" % ps, flush=True)
+    o, lse = pkg.flash_attn_decode_paged(*dev, max(lens))
+    torch.cuda.synchronize()
+    _compare(oracle, synth.BF16, host, ds, lens, o, lse, 1.0 / math.sqrt(128))
+
+
+def test_decode_cache_beyond_4gib(oracle):
+    """A pool of more than 5 GiB per cache whose sequences sit in its last
+    pages: every byte they read lies past 4 GiB from the pool's start.  The
+    pool's other pages are never written (uninitialised device memory) and
+    must never be read."""
+    lens = [300, 1025, 64]
+    hq, hkv, dqk, ps = 8, 2, 128, 64
+    host, ds, dev = _inputs(oracle, synth.BF16, lens, hq, hkv, dqk, ps, 4242)
+    page_bytes = ps * hkv * dqk * 2
+    pool = (5 << 30) // page_bytes + 16
+    used = dev[1].shape[0]
+    base = pool - used
+    print("decode with a pool of %d pages (%.2f GiB per cache), pages %d.. used" % (
+        pool, pool * page_bytes / 2.0 ** 30, base), flush=True)
+    kbig = torch.empty((pool, ps, hkv, dqk), dtype=torch.bfloat16, device=DEV)
+    vbig = torch.empty((pool, ps, hkv, 128), dtype=torch.bfloat16, device=DEV)
+    kbig[base:] = dev[1]
+    vbig[base:] = dev[2]
+    table = dev[3] + base
+    o, lse = pkg.flash_attn_decode_paged(dev[0], kbig, vbig, table, dev[4], max(lens))
+    torch.cuda.synchronize()
+    del kbig, vbig
+    _compare(oracle, synth.BF16, host, ds, lens, o, lse, 1.0 / math.sqrt(128))
