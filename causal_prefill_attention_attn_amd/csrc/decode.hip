@@ -32,17 +32,18 @@
 // (keys x heads, heads past G are zero columns).  In its accumulator, lane
 // group j (16 lanes) holds keys 4j .. 4j+3 of the tile and lane j*16 + g
 // holds head g, so each (lane group, head) pair runs its own online softmax
-// over its keys on the lane's four values.  The probabilities then go through
-// a wave-private LDS slot to the P.V layout, where lane group j holds the same
-// four keys' value rows and each lane 8 of the 128 output columns for every
-// head; P.V stays in fp32 on the vector ALU.  The 16 streams of a workgroup
-// are merged at the end.
+// over its keys on the lane's four values.  The probabilities then reach the
+// P.V layout by DPP row broadcasts (lane g of each 16-lane row to the whole
+// row), where lane group j holds the same four keys' value rows and each lane
+// 8 of the 128 output columns for every head; P.V stays in fp32 on the
+// vector ALU.  The 16 streams of a workgroup are merged at the end.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "attn_device.h"
 #include "attn_kernels.h"
@@ -246,6 +247,21 @@ __device__ __forceinline__ void decode_lds_wait(T& a, T& b, T& c, T& d, u32x4 (&
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(k[i]));
 }
 
+// x of lane g of the lane's 16-lane row (DPP row broadcast, no LDS)
+template <int g>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x150 + g, 0xF, 0xF, false));
+}
+template <int... gs>
+__device__ __forceinline__ void row_bcast_all(std::integer_sequence<int, gs...>, const f32x4& p,
+                                              float a, f32x4* pg, float* al) {
+  ((pg[gs] = f32x4{row_bcast<gs>(p[0]), row_bcast<gs>(p[1]), row_bcast<gs>(p[2]),
+                   row_bcast<gs>(p[3])},
+    al[gs] = row_bcast<gs>(a)),
+   ...);
+}
+
 template <int DQK, int G, bool kFP8>
 __global__ void __launch_bounds__(64 * kWaves)
 decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
@@ -259,10 +275,8 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   constexpr int kRing = decode_ring<DQK, G, kFP8>();
   constexpr int kQC = QT::kWords / 4;  // 16-byte chunks in a quarter row
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kWaves][kRing][LT::kBytes];
-  __shared__ f32x4 sP[kWaves][64];
-  __shared__ float sA[kWaves][64];
-  __shared__ float sM[kWaves][G], sL[kWaves][G];
-  static_assert(sizeof(float) * kWaves * G * kDV <= sizeof(ring), "merge buffer overlays the ring");
+  static_assert(sizeof(float) * kWaves * G * (kDV + 2) <= sizeof(ring),
+                "merge buffers overlay the ring");
 
   const int sp = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -370,17 +384,10 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(p[i] - mn);
     l_s = fmaf(l_s, alpha, (p[0] + p[1]) + (p[2] + p[3]));
     m_s = mn;
-    sP[wave][lane] = p;
-    sA[wave][lane] = alpha;
-    __builtin_amdgcn_wave_barrier();
+    // probabilities and rescale factor of head g's stream (lane 16 grp + g)
     f32x4 pg4[G];
     float al[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      pg4[g] = sP[wave][16 * grp + g];
-      al[g] = sA[wave][16 * grp + g];
-    }
-    __builtin_amdgcn_wave_barrier();
+    row_bcast_all(std::make_integer_sequence<int, G>{}, p, alpha, pg4, al);
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -440,14 +447,14 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
 
   // each lane of group grp takes the stream state of its group's G heads
   float m[G], l[G];
-  __builtin_amdgcn_wave_barrier();
-  sP[wave][lane] = f32x4{m_s, l_s, 0.0f, 0.0f};
-  __builtin_amdgcn_wave_barrier();
+  {
+    f32x4 st[G];
+    row_bcast_all(std::make_integer_sequence<int, G>{}, f32x4{m_s, l_s, 0.0f, 0.0f}, 0.0f, st, l);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const f32x4 st = sP[wave][16 * grp + g];
-    m[g] = st[0];
-    l[g] = st[1];
+    for (int g = 0; g < G; ++g) {
+      m[g] = st[g][0];
+      l[g] = st[g][1];
+    }
   }
 
   // merge the four lane groups of the wave (lanes sub, sub+16, sub+32, sub+48
@@ -475,6 +482,8 @@ decode_split_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   // the ring, which every wave has finished reading at the barrier
   __syncthreads();
   float (*sO)[G][kDV] = reinterpret_cast<float (*)[G][kDV]>(&ring[0][0][0]);
+  float (*sM)[G] = reinterpret_cast<float (*)[G]>(&ring[0][0][0] + sizeof(float) * kWaves * G * kDV);
+  float (*sL)[G] = sM + kWaves;
   if (grp == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
