@@ -135,3 +135,15 @@ def test_c5b_full_size_sampled_rows(oracle):
     o, lse = run_gpu(dev, w, ds)
     rows = synth.sample_rows(w.S, 256)
     check(oracle, w, enc, ds, o, lse, rows=rows)
+
+
+@pytest.mark.parametrize("d_qk", [128, 192])
+def test_non_causal_many_passes(oracle, d_qk):
+    """Non-causal at S = 4096: the interior loop runs whole passes of four
+    tiles many times with no mask; 256 sampled rows on every head."""
+    w = synth.Workload("bf16_nc4k_%d" % d_qk, 81, synth.BF16, 1, 4, 4096, d_qk, 128, "gaussian",
+                       "bf16 non-causal 4096")
+    print("case", w.name, flush=True)
+    enc, ds, dev = make_inputs(oracle, w)
+    o, lse = run_gpu(dev, w, ds, causal=False)
+    check(oracle, w, enc, ds, o, lse, rows=synth.sample_rows(w.S), causal=False)

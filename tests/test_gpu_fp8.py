@@ -135,3 +135,15 @@ def test_exact_p_full_size_sampled_rows(oracle):
     check(oracle, w, enc, ds, o, lse, rows=rows, exact_p=True)
     del dev, o, lse
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d_qk", [128, 192])
+def test_non_causal_many_passes(oracle, d_qk):
+    """Non-causal at S = 4096: every tile of every row is visible, so the
+    interior loop runs whole passes (eight or four tiles each) many times
+    with no mask; 256 sampled rows on every head against the oracle."""
+    w = _w("fp8_nc4k_%d" % d_qk, 1, 4, 4096, d_qk=d_qk, index=76)
+    print("case", w.name, flush=True)
+    enc, ds, dev = make_inputs(oracle, w)
+    o, lse = run_gpu(dev, w, ds, causal=False)
+    check(oracle, w, enc, ds, o, lse, rows=synth.sample_rows(w.S), causal=False)
