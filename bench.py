@@ -71,7 +71,7 @@ def parse():
                          "FP8 and BF16 at 32K, and C5 is the pages' MLA shape")
     ap.add_argument("--sub-energy", type=float, default=3.0,
                     help="sustained window (seconds) of each sub-record")
-    ap.add_argument("--det-launches", type=int, default=2000,
+    ap.add_argument("--det-launches", type=int, default=7200,
                     help="launches of the headline workload whose outputs are each compared "
                          "bitwise, on the device, with the first launch's (sub-records: a "
                          "tenth of it)")
