@@ -33,8 +33,11 @@
 //                   ds_read_b64_tr_b8 (16 lanes cooperatively read 8 rows of
 //                   16 bytes and each receives one column), B = P^T straight
 //                   from registers.
-// The running max m is refreshed when some row of the wave sees a larger
-// tile maximum (rescale skipped otherwise).  With m equal to the row max,
+// The running max m of a row is refreshed when it sees a larger tile
+// maximum, and only the lanes of the rows whose maximum grew multiply their
+// O and l (skipped when no row of the wave grew): the others would multiply
+// by exactly 1, and lanes masked off draw less power, which under the
+// board's power limit is returned as clock.  With m equal to the row max,
 // the row's largest probability becomes exactly 2^8 before rounding, so the
 // dominant weight of peaked rows is exact in e4m3.  (Refreshing only past a
 // threshold saves rescales but makes the top weight inexact: measured a few
@@ -389,12 +392,14 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
     for (int i = 2; i < 16; i += 2) mx1 = fmaxf(fmaxf(mx1, s[1][i]), s[1][i + 1]);
     return pair_max(fmaxf(mx0, mx1)) * c_log2;
   };
-  // running max refresh; O and l rescaled when some row's max grows
+  // running max refresh: the lanes of the rows whose max grew (and only
+  // those) take the new max and rescale O and l.  A per-lane branch: the
+  // region runs with EXEC set to those lanes and is skipped when there are
+  // none, with no vector instruction spent on the test beyond the compare.
   auto refresh = [&](float bmax) {
-    if (__any(bmax > m_run)) {
-      const float m_new = fmaxf(m_run, bmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+    if (bmax > m_run) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - bmax);
+      m_run = bmax;
 #pragma unroll
       for (int d = 0; d < kDV / 32; ++d)
 #pragma unroll
