@@ -425,10 +425,18 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       if (wave >= kIssuers) return;
 #pragma unroll
       for (int i = 0; i < kMine; ++i) {
-        if (i * kIssuers < kKL)
-          buffer_load_lds16(rk, &sm.k[st][lo_[i]], go[i] == 0xfffffff0u ? go[i] : kb0 + go[i]);
-        else
-          buffer_load_lds16(rv, &sm.v[st][lo_[i]], vb0 + go[i]);
+        // tiles of a pass lie inside the buffers: the tile's offset goes in
+        // the scalar offset field, except for d = 192 K rows, whose padding
+        // slots must read past the buffer (zeros)
+        if (i * kIssuers < kKL) {
+          if constexpr (LY::kKC * 16 == DQK * 2) {
+            buffer_load_lds16_so(rk, &sm.k[st][lo_[i]], go[i], kb0);
+          } else {
+            buffer_load_lds16(rk, &sm.k[st][lo_[i]], go[i] == 0xfffffff0u ? go[i] : kb0 + go[i]);
+          }
+        } else {
+          buffer_load_lds16_so(rv, &sm.v[st][lo_[i]], go[i], vb0);
+        }
       }
     };
     auto qk_c = [&](auto ST, f32x16* sc) {

@@ -98,6 +98,15 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base,
                                            16, (int)off, 0, 0, 0);
 }
+// The same with the wave-uniform part of the offset in the instruction's
+// scalar offset field, so that no vector add forms the address.  Only for
+// loads known to lie inside the buffer: the out-of-range zeros above are not
+// relied on here.
+__device__ __forceinline__ void buffer_load_lds16_so(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                                     uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base,
+                                           16, (int)voff, (int)soff, 0, 0);
+}
 
 // ds_read_b64_tr_b16 issued as inline assembly.  The compiler builtin for
 // it carries no alias information, so the wait-count pass makes every such

@@ -601,14 +601,19 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       if (wave >= kIssuers) return;
 #pragma unroll
       for (int i = 0; i < kMine; ++i) {
+        // every tile of a pass lies inside the buffers, so the tile's
+        // offset goes in the scalar offset field; at d = 192 the 4 padding
+        // slots of a 256-byte K row must read past the buffer (zeros), so
+        // those rows keep the whole offset in the bounds-checked part
         if (i * kIssuers < kKL) {
-          // K rows of 128 bytes fill their chunk slots; at d = 192 the 4
-          // padding slots of a 256-byte row read past the buffer (zeros)
-          const uint32_t g = LY::kKC * 16 == DQK ? kb + go[i]
-                                                 : (go[i] == 0xfffffff0u ? go[i] : kb + go[i]);
-          buffer_load_lds16(rk, &sm.k[buf][lo_[i]], g);
+          if constexpr (LY::kKC * 16 == DQK) {
+            buffer_load_lds16_so(rk, &sm.k[buf][lo_[i]], go[i], kb);
+          } else {
+            const uint32_t g = go[i] == 0xfffffff0u ? go[i] : kb + go[i];
+            buffer_load_lds16(rk, &sm.k[buf][lo_[i]], g);
+          }
         } else {
-          buffer_load_lds16(rv, &sm.v[buf][lo_[i]], vb + go[i]);
+          buffer_load_lds16_so(rv, &sm.v[buf][lo_[i]], go[i], vb);
         }
       }
     };
