@@ -108,6 +108,7 @@ struct Smem {
   using L = Layout<DQK, BN>;
   uint8_t k[kStages][L::kKBytes];
   uint8_t v[kStages][L::kVBytes];
+  uint8_t epi[kWaves][4096];  // per wave: its output rows on their way to memory
 };
 
 template <int DQK, int BN>
@@ -527,21 +528,10 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // ---- epilogue: O / l -> bf16, lse = ln2 * (m + log2 l)
   const float l_tot = lacc[0];
   const int qi = q0w + col;
-  if (qi < S) {
-    const float inv = 1.0f / l_tot;
-    __bf16* orow = o + ((sr.row0 + qi) * H + h) * kDV;
-#pragma unroll
-    for (int d = 0; d < kDV / 32; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[d][g * 4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + d * 32 + g * 8 + half * 4) = w;
-      }
-    if (lse != nullptr && half == 0)
-      lse[sr.lse0 + h * sr.lse_hs + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
-  }
+  store_rows_bf16<kDV>(oacc, 1.0f / l_tot, sm.epi[wave], o + ((sr.row0 + q0w) * H + h) * kDV,
+                       (int64_t)H * kDV, S - q0w, lane);
+  if (qi < S && lse != nullptr && half == 0)
+    lse[sr.lse0 + h * sr.lse_hs + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
 }
 
 }  // namespace

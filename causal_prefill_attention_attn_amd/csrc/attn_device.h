@@ -175,4 +175,49 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ u32x4 lds_load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+
+// One wave's 32 output rows to bf16 global memory through a 4 KB LDS area
+// that only this wave uses.  Lane (col, half) = (lane % 32, lane / 32)
+// holds, for row col, acc[d][4g + e] of column 32d + 8g + 4half + e
+// (d < DV/32, g < 4, e < 4), the transposed layout of the P.V accumulators.
+// Written straight from there, each 8-byte store instruction would touch 32
+// rows, i.e. 32 partly written 128-byte lines.  Instead, per round of 64
+// columns (128 bytes of a row) the wave writes its rows to LDS in 8-byte
+// pieces and reads them back 16 bytes per lane, eight lanes per row, so
+// that every store instruction writes 8 whole 128-byte row segments.  The
+// 16-byte chunk c of LDS row r sits at chunk c ^ (r & 7), so that the 8
+// lanes reading one row and the rows written together spread over the
+// banks.  Rows r >= nvalid are not stored; `orow0` is row 0's first column
+// and consecutive rows are `rstride` elements apart.
+template <int DV>
+__device__ __forceinline__ void store_rows_bf16(const f32x16* acc, float scale, uint8_t* area,
+                                                __bf16* orow0, int64_t rstride, int nvalid,
+                                                int lane) {
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  lds_u8* a = (lds_u8*)(uintptr_t)lds_addr(area);
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int rr = 0; rr < DV / 64; ++rr) {
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[2 * rr + dd][g * 4 + e] * scale);
+        const int ch = dd * 4 + g;
+        *(__attribute__((address_space(3))) bf16x4*)(a + col * 128 + ((ch ^ (col & 7)) << 4) +
+                                                     half * 8) = w;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (lane >> 3) + 8 * i, c = lane & 7;
+      const bf16x8 x = *(const __attribute__((address_space(3))) bf16x8*)(a + r * 128 +
+                                                                          ((c ^ (r & 7)) << 4));
+      if (r < nvalid) *reinterpret_cast<bf16x8*>(orow0 + r * rstride + rr * 64 + c * 8) = x;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
 }  // namespace cpattn

@@ -197,6 +197,7 @@ struct Smem {
   using L = Layout<DQK, BN>;
   uint8_t k[L::kStages][L::kKBytes];
   uint8_t v[L::kStages][L::kVBytes];
+  uint8_t epi[8][4096];  // per wave: its output rows on their way to memory
 };
 
 // One workgroup of 4*kOcc waves per compute unit (kOcc waves per SIMD),
@@ -224,6 +225,7 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
                     float v_descale, int causal, int rot_o) {
   using LY = Layout<DQK, BN>;
   constexpr int kWaves = 4 * kOcc;
+  static_assert(kWaves <= 8, "one 4 KB output staging area per wave");
   constexpr int kBM = 32 * kWaves;                 // query rows per workgroup
   constexpr int kSteps = DQK / 64;                 // 32x32x64 steps of Q.K^T
   constexpr int kKRowsPerLoad = 1024 / LY::kKPitch;
@@ -711,22 +713,12 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   if (rot_o) hadamard_o_rows(oacc, half);
   const float l_tot = l_run;
   const int qi = q0w + col;
-  if (qi < S) {
-    // 1/sqrt(128) normalises the rotation
-    const float inv = v_descale / l_tot * (rot_o ? 0.08838834764831845f : 1.0f);
-    __bf16* orow = o + ((sr.row0 + qi) * H + h) * kDV;
-#pragma unroll
-    for (int d = 0; d < kDV / 32; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[d][g * 4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + d * 32 + g * 8 + half * 4) = w;
-      }
-    if (lse != nullptr && half == 0)
-      lse[sr.lse0 + h * sr.lse_hs + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
-  }
+  // 1/sqrt(128) normalises the rotation
+  const float inv = v_descale / l_tot * (rot_o ? 0.08838834764831845f : 1.0f);
+  store_rows_bf16<kDV>(oacc, inv, sm.epi[wave], o + ((sr.row0 + q0w) * H + h) * kDV,
+                       (int64_t)H * kDV, S - q0w, lane);
+  if (qi < S && lse != nullptr && half == 0)
+    lse[sr.lse0 + h * sr.lse_hs + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
 }
 
 }  // namespace
