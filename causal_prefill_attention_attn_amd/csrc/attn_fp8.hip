@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(256 * kOcc, 1)
 attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                     const uint8_t* __restrict__ v, __bf16* __restrict__ o,
                     float* __restrict__ lse, const int32_t* __restrict__ cu, int64_t total,
-                    int S_max, int H, int BH, int nqb, float c_log2,
+                    int S_max, int H, int BH, int nqb, float c_log2, float c8n,
                     float v_descale, int causal, int rot_o) {
   using LY = Layout<DQK, BN>;
   constexpr int kWaves = 4 * kOcc;
@@ -409,7 +409,6 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
       l_run *= alpha;
     }
   };
-  const float c8n = 8.0f * c_log2 * (256.0f / 65535.0f);
   // P = e4m3(2^(c*s - m + k)); k = 8 - ceil(block max - m) puts the block
   // maximum in (2^7, 2^8]; k >= 0 since block max <= m after the refresh
   auto probs = [&](const f32x16* scur, float bmax, int& pscale) {
@@ -733,11 +732,15 @@ int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float*
   const int BH = B * H;
   const dim3 grid((unsigned)nqb * (unsigned)BH);
   const float c_log2 = softmax_scale * q_descale * k_descale * 1.4426950408889634f;
+  // the lean code's scale 8 c in units of the 16-bit normalised conversion,
+  // passed in so that its 32 FMAs per tile read it from a scalar register
+  // (the scalar unit has no float multiply to form it in the kernel)
+  const float c8n = 8.0f * c_log2 * (256.0f / 65535.0f);
   const bool lean = !exact_p;  // probabilities: lean (default) or exact exp2 + convert
 #define CPATTN_LAUNCH_FP8(DQK, BN, LEAN, OCC)                                                     \
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, BN, LEAN, OCC>), grid, dim3(256 * OCC), 0, stream, \
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, cu, \
-                     total, S, H, BH, nqb, c_log2, v_descale, causal, (int)rot_o)
+                     total, S, H, BH, nqb, c_log2, c8n, v_descale, causal, (int)rot_o)
   if (d_qk == 128) {
     if (lean) CPATTN_LAUNCH_FP8(128, 64, true, 2);
     else CPATTN_LAUNCH_FP8(128, 64, false, 2);
