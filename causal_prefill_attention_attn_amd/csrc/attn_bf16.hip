@@ -528,8 +528,8 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // ---- epilogue: O / l -> bf16, lse = ln2 * (m + log2 l)
   const float l_tot = lacc[0];
   const int qi = q0w + col;
-  store_rows_bf16<kDV>(oacc, 1.0f / l_tot, sm.epi[wave], o + ((sr.row0 + q0w) * H + h) * kDV,
-                       (int64_t)H * kDV, S - q0w, lane);
+  store_rows_bf16<kDV>(oacc, 1.0f / l_tot, sm.epi[wave], o, sr.row0 + q0w, (int64_t)H * kDV,
+                       (int64_t)h * kDV, S - q0w, lane);
   if (qi < S && lse != nullptr && half == 0)
     lse[sr.lse0 + h * sr.lse_hs + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
 }

@@ -187,12 +187,13 @@ __device__ __forceinline__ u32x4 lds_load16(const void* p) {
 // that every store instruction writes 8 whole 128-byte row segments.  The
 // 16-byte chunk c of LDS row r sits at chunk c ^ (r & 7), so that the 8
 // lanes reading one row and the rows written together spread over the
-// banks.  Rows r >= nvalid are not stored; `orow0` is row 0's first column
-// and consecutive rows are `rstride` elements apart.
+// banks.  Row r of the wave is output row row0 + r, which starts at element
+// (row0 + r) * rstride + col0 of o; rows r >= nvalid are not stored (nor
+// their addresses formed).
 template <int DV>
 __device__ __forceinline__ void store_rows_bf16(const f32x16* acc, float scale, uint8_t* area,
-                                                __bf16* orow0, int64_t rstride, int nvalid,
-                                                int lane) {
+                                                __bf16* o, int64_t row0, int64_t rstride,
+                                                int64_t col0, int nvalid, int lane) {
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   lds_u8* a = (lds_u8*)(uintptr_t)lds_addr(area);
   const int col = lane & 31, half = lane >> 5;
@@ -215,7 +216,8 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16* acc, float scale, 
       const int r = (lane >> 3) + 8 * i, c = lane & 7;
       const bf16x8 x = *(const __attribute__((address_space(3))) bf16x8*)(a + r * 128 +
                                                                           ((c ^ (r & 7)) << 4));
-      if (r < nvalid) *reinterpret_cast<bf16x8*>(orow0 + r * rstride + rr * 64 + c * 8) = x;
+      if (r < nvalid)
+        *reinterpret_cast<bf16x8*>(o + (row0 + r) * rstride + col0 + rr * 64 + c * 8) = x;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }

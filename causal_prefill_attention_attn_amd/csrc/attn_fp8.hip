@@ -714,8 +714,8 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int qi = q0w + col;
   // 1/sqrt(128) normalises the rotation
   const float inv = v_descale / l_tot * (rot_o ? 0.08838834764831845f : 1.0f);
-  store_rows_bf16<kDV>(oacc, inv, sm.epi[wave], o + ((sr.row0 + q0w) * H + h) * kDV,
-                       (int64_t)H * kDV, S - q0w, lane);
+  store_rows_bf16<kDV>(oacc, inv, sm.epi[wave], o, sr.row0 + q0w, (int64_t)H * kDV,
+                       (int64_t)h * kDV, S - q0w, lane);
   if (qi < S && lse != nullptr && half == 0)
     lse[sr.lse0 + h * sr.lse_hs + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
 }
