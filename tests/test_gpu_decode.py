@@ -63,9 +63,11 @@ def _compare(oracle, dtype, host, ds, lens, o, lse, tau):
 
 @pytest.mark.parametrize("dtype", [synth.BF16, synth.FP8])
 # every (d_qk, G = hq / hkv) kernel instance: G = 1, 2, 4, 8 at d_qk 128 and 192
+# (and larger pages: 256 and 1024 keys, a split inside one page)
 @pytest.mark.parametrize("dqk,hq,hkv,ps", [(128, 2, 2, 16), (128, 4, 2, 32), (128, 8, 2, 64),
                                            (128, 16, 2, 32), (192, 2, 2, 32), (192, 4, 2, 16),
-                                           (192, 16, 4, 64), (192, 8, 1, 128)])
+                                           (192, 16, 4, 64), (192, 8, 1, 128), (128, 4, 2, 256),
+                                           (192, 8, 2, 1024)])
 def test_decode_matches_oracle(oracle, dtype, dqk, hq, hkv, ps):
     lens = [0, 1, 15, 16, 17, 300, 1025, 2000]
     host, ds, dev = _inputs(oracle, dtype, lens, hq, hkv, dqk, ps, 100 + dqk + hq + ps + dtype)
