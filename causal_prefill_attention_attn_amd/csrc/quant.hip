@@ -14,17 +14,32 @@
 namespace cpattn {
 namespace {
 
-__global__ void __launch_bounds__(256) amax_kernel(const float* __restrict__ x, int64_t n,
+// magnitude of a float as a bit pattern: non-negative floats order like
+// unsigned integers, so the max is exact, order-free and needs no float
+// compare; NaN patterns (above the infinity pattern) count as zero
+__device__ __forceinline__ uint32_t mag_bits(float v) {
+  const uint32_t a = __float_as_uint(v) & 0x7fffffffu;
+  return a <= 0x7f800000u ? a : 0u;
+}
+
+// vec: x is 16-byte aligned, and each thread reads four floats per load
+// (the scalar loop takes the elements past the last whole group of four)
+__global__ void __launch_bounds__(256) amax_kernel(const float* __restrict__ x, int64_t n, int vec,
                                                    uint32_t* __restrict__ out) {
-  // magnitudes as bit patterns: non-negative floats order like unsigned
-  // integers, so the max is exact, order-free and needs no float compare;
-  // NaN patterns (above the infinity pattern) are skipped
   uint32_t m = 0u;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const uint32_t a = __float_as_uint(x[i]) & 0x7fffffffu;
-    m = max(m, a <= 0x7f800000u ? a : 0u);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t tail = 0;
+  if (vec) {
+    const int64_t n4 = n >> 2;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    for (int64_t i = i0; i < n4; i += stride) {
+      const float4 v = x4[i];
+      m = max(max(m, max(mag_bits(v.x), mag_bits(v.y))), max(mag_bits(v.z), mag_bits(v.w)));
+    }
+    tail = n4 << 2;
   }
+  for (int64_t i = tail + i0; i < n; i += stride) m = max(m, mag_bits(x[i]));
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   __shared__ uint32_t wmax[4];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
@@ -34,14 +49,38 @@ __global__ void __launch_bounds__(256) amax_kernel(const float* __restrict__ x, 
 
 // descale from device memory when dptr is set (the whole quantization then
 // runs without a host round trip), else the argument
+// vec: x and out are 16-byte aligned, and each thread encodes 16
+// consecutive values per step (four 16-byte loads, one 16-byte store); the
+// scalar loop takes the elements past the last whole group of 16
 __global__ void __launch_bounds__(256) quantize_kernel(const float* __restrict__ x, int64_t n,
-                                                       const float* __restrict__ dptr,
+                                                       int vec, const float* __restrict__ dptr,
                                                        float dval, uint8_t* __restrict__ out) {
   const float descale = dptr != nullptr ? *dptr : dval;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    out[i] = e4m3_from_f32(x[i] / descale);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t tail = 0;
+  if (vec) {
+    const int64_t n16 = n >> 4;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    uint4* o16 = reinterpret_cast<uint4*>(out);
+    for (int64_t i = i0; i < n16; i += stride) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = x4[4 * i + q];
+        w[q] = (uint32_t)e4m3_from_f32(v.x / descale) |
+               ((uint32_t)e4m3_from_f32(v.y / descale) << 8) |
+               ((uint32_t)e4m3_from_f32(v.z / descale) << 16) |
+               ((uint32_t)e4m3_from_f32(v.w / descale) << 24);
+      }
+      o16[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    tail = n16 << 4;
+  }
+  for (int64_t i = tail + i0; i < n; i += stride) out[i] = e4m3_from_f32(x[i] / descale);
 }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // The per-tensor scale rule of the FP8 quantization, in place: *p holds
 // amax (as written by the amax kernels) and becomes amax / 448 in fp32, or
@@ -58,19 +97,30 @@ __global__ void descale_from_amax(float* p) {
 
 int launch_amax_f32(const float* x, int64_t n, float* amax_out, hipStream_t stream) {
   hipLaunchKernelGGL(zero_u32, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(amax_out));
-  int64_t blocks = (n + 255) / 256;
+  const int vec = aligned16(x) ? 1 : 0;
+  int64_t blocks = (n / (vec ? 4 : 1) + 255) / 256;
+  if (blocks < 1) blocks = 1;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n,
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, vec,
                      reinterpret_cast<uint32_t*>(amax_out));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+namespace {
+void launch_quantize(const float* x, int64_t n, const float* dptr, float dval, uint8_t* out,
+                     hipStream_t stream) {
+  const int vec = aligned16(x) && aligned16(out) ? 1 : 0;
+  int64_t blocks = (n / (vec ? 16 : 1) + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, vec,
+                     dptr, dval, out);
+}
+}  // namespace
+
 int launch_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out,
                          hipStream_t stream) {
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n,
-                     (const float*)nullptr, descale, out);
+  launch_quantize(x, n, nullptr, descale, out, stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -83,10 +133,7 @@ int launch_quantize_fp8(const float* x, int64_t rows, int d, bool rotate, uint8_
   hipLaunchKernelGGL(descale_from_amax, dim3(1), dim3(64), 0, stream, descale);
   if (hipGetLastError() != hipSuccess) return -1;
   if (rotate) return launch_hadamard_quantize_dev(x, rows, d, descale, codes, stream);
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n,
-                     (const float*)descale, 1.0f, codes);
+  launch_quantize(x, n, descale, 1.0f, codes, stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -159,6 +159,48 @@ def test_fused_rotation_quantization(oracle, d):
     assert diff.max() <= 1 and (diff > 0).mean() <= 1e-3
 
 
+@pytest.mark.parametrize("d", [128, 192])
+def test_both_layouts_give_the_same_bits(oracle, d):
+    """16-byte-aligned buffers take the 16-elements-per-thread kernels, other
+    buffers the row-per-wave ones; both run the same butterflies in the same
+    order, so rotation (fp32 and bf16), rotated amax and fused codes agree
+    bit for bit between an aligned copy and a copy offset by one element."""
+    rng = np.random.default_rng(d + 11)
+    rows = 515
+    x = (rng.standard_normal((rows, d)) * np.exp(rng.standard_normal(d))).astype(np.float32)
+    n = rows * d
+    st = torch.cuda.current_stream().cuda_stream
+    for esz, dt in ((4, torch.float32), (2, torch.bfloat16)):
+        a_in = torch.from_numpy(x.reshape(-1)).to(DEV).to(dt)
+        src = torch.zeros((n + 8,), dtype=dt, device=DEV)
+        src[1:n + 1] = a_in
+        u_in = src[1:n + 1]
+        a_out = torch.empty((n,), dtype=dt, device=DEV)
+        u_buf = torch.empty((n + 8,), dtype=dt, device=DEV)
+        fn = pkg.attn_hadamard_f32 if esz == 4 else pkg.attn_hadamard_bf16
+        assert fn(a_in.data_ptr(), rows, d, a_out.data_ptr(), st) == 0
+        assert fn(u_in.data_ptr(), rows, d, u_buf.data_ptr() + esz, st) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(a_out.view(torch.int16 if esz == 2 else torch.int32),
+                           u_buf[1:n + 1].view(torch.int16 if esz == 2 else torch.int32)), esz
+        if esz == 4:
+            ref = oracle.hadamard(x).reshape(-1)
+            assert np.abs(a_out.cpu().numpy() - ref).max() <= 1e-6 * np.abs(ref).max()
+            am = torch.empty((2,), dtype=torch.float32, device=DEV)
+            assert pkg.attn_hadamard_amax_f32(a_in.data_ptr(), rows, d, am.data_ptr(), st) == 0
+            assert pkg.attn_hadamard_amax_f32(u_in.data_ptr(), rows, d, am.data_ptr() + 4, st) == 0
+            ca = torch.empty((n,), dtype=torch.uint8, device=DEV)
+            cu = torch.empty((n + 16,), dtype=torch.uint8, device=DEV)
+            assert pkg.attn_hadamard_quantize_e4m3(a_in.data_ptr(), rows, d, 0.01, ca.data_ptr(),
+                                                   st) == 0
+            assert pkg.attn_hadamard_quantize_e4m3(u_in.data_ptr(), rows, d, 0.01,
+                                                   cu.data_ptr() + 3, st) == 0
+            torch.cuda.synchronize()
+            assert am[0].item() == am[1].item() == float(np.abs(a_out.cpu().numpy()).max())
+            assert torch.equal(ca, cu[3:n + 3])
+            assert np.array_equal(ca.cpu().numpy(), oracle.quantize_e4m3(a_out.cpu().numpy(), 0.01))
+
+
 def _gpu_fp8_fused(xs, tau):
     """Rotate and quantize Q, K, V; attention with the O rotation fused into
     the kernel's epilogue (attn_fwd_ex with ATTN_FLAG_HADAMARD_O)."""
