@@ -440,13 +440,18 @@ def time_hadamard(w, host, pkg, torch, stream, attn_ms, dev_in, ds, reps=10):
     (amax pass + encode pass) of Q, K, V against the fused rotate+quantize
     passes, the standalone rotation of O (bf16) that undoes a rotated V, and
     the attention itself with that O rotation fused into its epilogue (FP8).
-    Rates count one read of the input per pass and one write of the codes."""
+    Rates count one read of the input per pass and one write of the codes.
+    A pass over a small tensor can take less time than the host needs to
+    issue it, so every rep is queued behind a ~20 ms spin kernel before the
+    start event runs: the events then bracket GPU time only."""
     dev = torch.device("cuda:0")
 
     def timed(fn):
         fn()
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(40_000_000)
         s.record(stream)
         for _ in range(reps):
             fn()

@@ -82,12 +82,12 @@ __global__ void __launch_bounds__(256) hadamard_kernel(const void* x, int64_t ro
   }
 }
 
-// amax of the rotated rows (magnitudes as bit patterns, as in quant.hip);
-// *out must be zero on entry
+// amax of the rotated rows (magnitudes as bit patterns); *out must be zero
+// on entry
 template <int D>
-__global__ void __launch_bounds__(256) hadamard_amax_kernel(const float* __restrict__ x,
-                                                            int64_t rows,
-                                                            uint32_t* __restrict__ out) {
+__global__ void __launch_bounds__(kAmaxThreads) hadamard_amax_kernel(const float* __restrict__ x,
+                                                                     int64_t rows,
+                                                                     uint32_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
   uint32_t m = 0u;
@@ -96,16 +96,9 @@ __global__ void __launch_bounds__(256) hadamard_amax_kernel(const float* __restr
     float v[D / 64];
     rotate_row<D, false>(x, r, lane, v);
 #pragma unroll
-    for (int j = 0; j < D / 64; ++j) {
-      const uint32_t a = __float_as_uint(v[j]) & 0x7fffffffu;
-      m = max(m, a <= 0x7f800000u ? a : 0u);
-    }
+    for (int j = 0; j < D / 64; ++j) m = max(m, mag_bits(v[j]));
   }
-  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  __shared__ uint32_t wmax[4];
-  if (lane == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) atomicMax(out, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+  amax_commit(m, out);
 }
 
 // e4m3 codes of the rotated rows divided by descale (read from device memory
@@ -276,9 +269,9 @@ __global__ void __launch_bounds__(256) hadamard16_kernel(const void* x, int64_t 
 }
 
 template <int BK>
-__global__ void __launch_bounds__(256) hadamard16_amax_kernel(const float* __restrict__ x,
-                                                              int64_t groups,
-                                                              uint32_t* __restrict__ out) {
+__global__ void __launch_bounds__(kAmaxThreads) hadamard16_amax_kernel(const float* __restrict__ x,
+                                                                       int64_t groups,
+                                                                       uint32_t* __restrict__ out) {
   constexpr int CH = kChF32;
   const int lane = threadIdx.x & 63;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -288,16 +281,9 @@ __global__ void __launch_bounds__(256) hadamard16_amax_kernel(const float* __res
     load16<BK, CH, false>(x, g, v);
     rotate16<BK, CH>(v, lane);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t a = __float_as_uint(v[e]) & 0x7fffffffu;
-      m = max(m, a <= 0x7f800000u ? a : 0u);
-    }
+    for (int e = 0; e < 16; ++e) m = max(m, mag_bits(v[e]));
   }
-  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  __shared__ uint32_t wmax[4];
-  if (lane == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) atomicMax(out, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+  amax_commit(m, out);
 }
 
 template <int BK>
@@ -380,14 +366,16 @@ int launch_hadamard_amax(const float* x, int64_t rows, int d, float* amax_out,
   hipLaunchKernelGGL(zero_u32, dim3(1), dim3(1), 0, stream, out);
   if (aligned16(x)) {
     const int64_t groups = rows * d / 16;
-    const dim3 grid(grid16(groups)), block(256);
+    int64_t blocks = (groups + kAmaxThreads - 1) / kAmaxThreads;
+    const dim3 grid((unsigned)(blocks > kAmaxBlocks ? kAmaxBlocks : blocks)), block(kAmaxThreads);
     if (d == 128)
       hipLaunchKernelGGL(hadamard16_amax_kernel<128>, grid, block, 0, stream, x, groups, out);
     else
       hipLaunchKernelGGL(hadamard16_amax_kernel<64>, grid, block, 0, stream, x, groups, out);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  const dim3 grid(hadamard_grid(rows)), block(256);
+  const int64_t blocks = (rows + kAmaxThreads / 64 - 1) / (kAmaxThreads / 64);  // a row per wave
+  const dim3 grid((unsigned)(blocks > kAmaxBlocks ? kAmaxBlocks : blocks)), block(kAmaxThreads);
   if (d == 128) hipLaunchKernelGGL(hadamard_amax_kernel<128>, grid, block, 0, stream, x, rows, out);
   else hipLaunchKernelGGL(hadamard_amax_kernel<192>, grid, block, 0, stream, x, rows, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;

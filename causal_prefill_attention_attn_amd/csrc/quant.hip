@@ -14,37 +14,33 @@
 namespace cpattn {
 namespace {
 
-// magnitude of a float as a bit pattern: non-negative floats order like
-// unsigned integers, so the max is exact, order-free and needs no float
-// compare; NaN patterns (above the infinity pattern) count as zero
-__device__ __forceinline__ uint32_t mag_bits(float v) {
-  const uint32_t a = __float_as_uint(v) & 0x7fffffffu;
-  return a <= 0x7f800000u ? a : 0u;
-}
-
-// vec: x is 16-byte aligned, and each thread reads four floats per load
-// (the scalar loop takes the elements past the last whole group of four)
-__global__ void __launch_bounds__(256) amax_kernel(const float* __restrict__ x, int64_t n, int vec,
-                                                   uint32_t* __restrict__ out) {
+// Largest magnitude (as a bit pattern) of x, folded into *out.  vec: x is
+// 16-byte aligned and each thread has four 16-byte loads in flight per step
+// (coalesced across the block); the scalar loop takes the elements past the
+// last whole group of four, or all of them when x is not aligned.
+__global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const float* __restrict__ x, int64_t n,
+                                                            int vec, uint32_t* __restrict__ out) {
   uint32_t m = 0u;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t tail = 0;
   if (vec) {
     const int64_t n4 = n >> 2;
     const float4* x4 = reinterpret_cast<const float4*>(x);
-    for (int64_t i = i0; i < n4; i += stride) {
-      const float4 v = x4[i];
-      m = max(max(m, max(mag_bits(v.x), mag_bits(v.y))), max(mag_bits(v.z), mag_bits(v.w)));
+    for (int64_t i = i0; i < n4; i += 4 * stride) {
+      float4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[q] = i + q * stride < n4 ? x4[i + q * stride] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        m = max(max(m, max(mag_bits(v[q].x), mag_bits(v[q].y))),
+                max(mag_bits(v[q].z), mag_bits(v[q].w)));
     }
     tail = n4 << 2;
   }
   for (int64_t i = tail + i0; i < n; i += stride) m = max(m, mag_bits(x[i]));
-  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  __shared__ uint32_t wmax[4];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) atomicMax(out, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+  amax_commit(m, out);
 }
 
 // descale from device memory when dptr is set (the whole quantization then
@@ -98,10 +94,10 @@ __global__ void descale_from_amax(float* p) {
 int launch_amax_f32(const float* x, int64_t n, float* amax_out, hipStream_t stream) {
   hipLaunchKernelGGL(zero_u32, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(amax_out));
   const int vec = aligned16(x) ? 1 : 0;
-  int64_t blocks = (n / (vec ? 4 : 1) + 255) / 256;
+  int64_t blocks = (n / (vec ? 16 : 1) + kAmaxThreads - 1) / kAmaxThreads;
   if (blocks < 1) blocks = 1;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, n, vec,
+  if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, x, n, vec,
                      reinterpret_cast<uint32_t*>(amax_out));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
