@@ -323,12 +323,20 @@ def test_hadamard_rows_are_isometric_and_self_inverse(oracle, d):
     y = oracle.hadamard(x)
     np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
     np.testing.assert_allclose(oracle.hadamard(y), x, rtol=0, atol=1e-13)
-    # block structure: a unit vector in block b spreads only over block b
-    n = oracle.hadamard_block(d)
-    e = np.zeros(d)
-    e[d - 1] = 1.0
-    r = oracle.hadamard(e)
-    assert np.all(r[: d - n] == 0) and np.allclose(np.abs(r[d - n:]), 1 / math.sqrt(n))
+    # block structure, as read: one block of 128 at d = 128, three blocks of
+    # 64 at d = 192.  A unit vector in a block spreads, with equal
+    # magnitudes 1/sqrt(block), over that block and nowhere else.
+    n = {128: 128, 192: 64}[d]
+    assert oracle.hadamard_block(d) == n
+    for c in (0, n - 1, d - n, d - 1):
+        e = np.zeros(d)
+        e[c] = 1.0
+        r = oracle.hadamard(e)
+        lo = (c // n) * n
+        inside = np.zeros(d, bool)
+        inside[lo:lo + n] = True
+        assert np.all(r[~inside] == 0), c
+        np.testing.assert_allclose(np.abs(r[inside]), 1 / math.sqrt(n), rtol=1e-15)
 
 
 def test_hadamard_spreads_an_outlier_channel(oracle):
