@@ -108,18 +108,20 @@ def test_quantize_fp8_all_zero():
 
 @pytest.mark.parametrize("x_off,o_off", [(0, 0), (1, 0), (0, 3), (2, 5)])
 def test_quantize_and_amax_alignment_and_tails(oracle, x_off, o_off):
-    """Aligned buffers take a vector path (16 values per thread, whole groups
-    only) and the rest a scalar one; every length from 1 to 70 and both
-    alignments give the oracle's codes and amax exactly; length 0 is refused."""
+    """Aligned buffers take vector paths (whole runs of 1024 values a wave at
+    a time, then groups of 16 values per thread) and the rest a scalar loop;
+    every length from 1 to 70, lengths around whole runs, and both
+    alignments give the oracle's codes and amax exactly; length 0 is
+    refused."""
     rng = np.random.default_rng(7 + x_off + 10 * o_off)
-    base = (rng.standard_normal(128) * 40).astype(np.float32)
+    base = (rng.standard_normal(6000) * 40).astype(np.float32)
     tb = torch.from_numpy(base).to(DEV)
-    ob = torch.empty((128,), dtype=torch.uint8, device=DEV)
+    ob = torch.empty((6000,), dtype=torch.uint8, device=DEV)
     amax = torch.empty((1,), dtype=torch.float32, device=DEV)
     st = torch.cuda.current_stream().cuda_stream
     assert pkg.attn_quantize_e4m3(tb.data_ptr(), 0, 1.0, ob.data_ptr(), st) != 0
     assert pkg.attn_amax_f32(tb.data_ptr(), 0, amax.data_ptr(), st) != 0
-    for n in range(1, 71):
+    for n in list(range(1, 71)) + [1008, 1023, 1024, 1025, 1040, 2047, 2048 + 16 + 3, 5003]:
         x = base[x_off:x_off + n]
         ob.fill_(0xAA)
         assert pkg.attn_quantize_e4m3(tb.data_ptr() + 4 * x_off, n, 0.37, ob.data_ptr() + o_off,
