@@ -415,7 +415,6 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // every stage index and LDS address offset is a compile-time constant
     // (no per-tile address or stage arithmetic), and every tile issued ahead
     // exists (t + 6 < nkt), so no load is tested.
-    typedef const __attribute__((address_space(3))) uint8_t* lds_u8;
     const uint32_t kx0 = lds_addr(sm.k[0]);
     const uint32_t vx0 = lds_addr(sm.v[0]);
     auto issue_c = [&](auto J, int t0) {  // tile t0 + J + 3 into stage (J + 3) % 4
