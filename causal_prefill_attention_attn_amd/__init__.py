@@ -19,7 +19,7 @@ import os
 
 __all__ = [
     "ATTN_DTYPE_BF16", "ATTN_DTYPE_FP8", "AttnError", "lib_path", "load_library",
-    "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_amax_f32", "attn_quantize_e4m3",
+    "attn_fwd", "attn_fwd_ex", "attn_fwd_balanced", "attn_fwd_varlen", "attn_amax_f32", "attn_quantize_e4m3",
     "attn_quantize_fp8", "attn_status_string",
     "attn_version", "attn_hadamard_f32", "attn_hadamard_bf16", "attn_hadamard_amax_f32",
     "attn_hadamard_quantize_e4m3", "attn_decode_paged", "attn_decode_paged_noalloc",
@@ -69,6 +69,8 @@ def load_library():
     lib.attn_fwd_ex.restype = i32
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, i32,
                                 f32, f32, f32, ctypes.c_uint32, vp]
+    lib.attn_fwd_balanced.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, i32,
+                                      i32, f32, f32, f32, ctypes.c_uint32, vp, vp]
     lib.attn_fwd_varlen.restype = i32
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32,
                                     i32, i32, f32, f32, f32, vp]
@@ -119,6 +121,14 @@ def attn_fwd_ex(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale, causal, dtyp
     return int(load_library().attn_fwd_ex(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale,
                                           causal, dtype, q_descale, k_descale, v_descale, flags,
                                           stream))
+
+
+def attn_fwd_balanced(q, k, v, o, lse, B, S, H, d_qk, d_v, softmax_scale, causal, dtype,
+                      q_descale=1.0, k_descale=1.0, v_descale=1.0, flags=0, counter=None,
+                      stream=None) -> int:
+    return int(load_library().attn_fwd_balanced(q, k, v, o, lse, B, S, H, d_qk, d_v,
+                                                softmax_scale, causal, dtype, q_descale,
+                                                k_descale, v_descale, flags, counter, stream))
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, n_seqs, total, max_seqlen, H, d_qk, d_v,
@@ -223,7 +233,7 @@ def _element_dtype(t) -> int:
 
 def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_descale=1.0,
                     v_descale=1.0, out=None, lse=None, return_lse=True, hadamard_o=False,
-                    exact_p=False):
+                    exact_p=False, balanced=True):
     """Forward attention on [B, S, H, D] tensors.
 
     q, k: [B, S, H, d_qk]; v: [B, S, H, d_v]; all bfloat16, or all FP8 e4m3
@@ -231,9 +241,12 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_d
     ``hadamard_o`` (FP8): rows of O are multiplied by the normalised Hadamard
     matrix, undoing a V rotated before quantization (``quantize_fp8(v,
     rotate=True)``).  ``exact_p`` (FP8): probabilities by exp2 and a rounding
-    conversion instead of the lean form.  Returns ``(o, lse)``: o bfloat16
-    [B, S, H, d_v], lse float32 [B, H, S] (natural log); lse is None when
-    ``return_lse`` is False.
+    conversion instead of the lean form.  ``balanced`` (default): the call
+    goes through attn_fwd_balanced with a one-word counter from torch's
+    allocator, so that the shortest query blocks are shared among the XCDs
+    as they free up (same results bit for bit); False calls attn_fwd_ex.
+    Returns ``(o, lse)``: o bfloat16 [B, S, H, d_v], lse float32 [B, H, S]
+    (natural log); lse is None when ``return_lse`` is False.
     """
     torch = _torch()
     dt = _element_dtype(q)
@@ -261,13 +274,16 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, q_descale=1.0, k_d
         lse = None
     if lse is not None:
         _check_buffer("lse", lse, (B, H, S), torch.float32, q.device)
-    st = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                     lse.data_ptr() if lse is not None else None, B, S, H, d_qk, d_v,
-                     float(softmax_scale), int(bool(causal)), dt, float(q_descale),
-                     float(k_descale), float(v_descale),
-                     (1 if hadamard_o else 0) | (2 if exact_p else 0),
-                     _stream_handle(q.device))
-    _check(st, "attn_fwd_ex")
+    # a fresh word per call: torch's allocator orders its reuse on the stream
+    counter = torch.empty((1,), dtype=torch.int32, device=q.device) if balanced else None
+    st = attn_fwd_balanced(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr() if lse is not None else None, B, S, H, d_qk, d_v,
+                           float(softmax_scale), int(bool(causal)), dt, float(q_descale),
+                           float(k_descale), float(v_descale),
+                           (1 if hadamard_o else 0) | (2 if exact_p else 0),
+                           counter.data_ptr() if counter is not None else None,
+                           _stream_handle(q.device))
+    _check(st, "attn_fwd_balanced")
     return out, lse
 
 

@@ -34,8 +34,8 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_DTYPE: return "dtype must be ATTN_DTYPE_BF16 (0) or ATTN_DTYPE_FP8 (1)";
     case ATTN_ERR_UNSUPPORTED: return "unsupported (d_qk, d_v) (want (128,128) or (192,128)) or causal not 0/1";
     case ATTN_ERR_SCALE: return "softmax_scale and the FP8 descales must be finite and > 0";
-    case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case ATTN_ERR_ALIAS: return "o or lse overlaps an input or the other output";
+    case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned; lse, cu_seqlens and the counter 4-byte aligned";
+    case ATTN_ERR_ALIAS: return "o, lse or the counter overlaps an input or another output";
     case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes";
     case ATTN_ERR_SCRATCH: return "the step needs more than the library's static decode scratch (ATTN_DECODE_SCRATCH_BYTES)";
@@ -53,7 +53,7 @@ namespace {
 int fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu,
         int64_t total, int64_t B, int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale,
         int causal, int dtype, float q_descale, float k_descale, float v_descale, unsigned flags,
-        void* stream) {
+        int32_t* counter, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B < 1 || S < 1 || H < 1 || total < 1) return ATTN_ERR_SHAPE;
   // 32-bit indices inside the kernels: rows, heads, problem*head and the grid
@@ -72,7 +72,7 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, const 
       !(finite_positive(q_descale) && finite_positive(k_descale) && finite_positive(v_descale)))
     return ATTN_ERR_SCALE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      (lse && !aligned(lse, 4)) || (cu && !aligned(cu, 4)))
+      (lse && !aligned(lse, 4)) || (cu && !aligned(cu, 4)) || (counter && !aligned(counter, 4)))
     return ATTN_ERR_ALIGN;
   const int64_t esz = dtype == ATTN_DTYPE_BF16 ? 2 : 1;
   // the kernels address one problem of q/k/v with 32-bit byte offsets (plus
@@ -87,17 +87,21 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, const 
     return ATTN_ERR_ALIAS;
   if (cu && (overlap(cu, (B + 1) * 4, o, no) || (lse && overlap(cu, (B + 1) * 4, lse, nl))))
     return ATTN_ERR_ALIAS;
+  if (counter && (overlap(counter, 4, q, nq) || overlap(counter, 4, k, nq) ||
+                  overlap(counter, 4, v, nv) || overlap(counter, 4, o, no) ||
+                  (lse && overlap(counter, 4, lse, nl))))
+    return ATTN_ERR_ALIAS;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int rc;
   if (dtype == ATTN_DTYPE_BF16)
     rc = cpattn::launch_attn_bf16(q, k, v, o, lse, cu, total, (int)B, (int)S, (int)H, d_qk,
-                                  softmax_scale, causal, st);
+                                  softmax_scale, causal, counter, st);
   else
     rc = cpattn::launch_attn_fp8(q, k, v, o, lse, cu, total, (int)B, (int)S, (int)H, d_qk,
                                  softmax_scale, causal, q_descale, k_descale, v_descale,
                                  (flags & ATTN_FLAG_HADAMARD_O) != 0,
-                                 (flags & ATTN_FLAG_EXACT_P) != 0, st);
+                                 (flags & ATTN_FLAG_EXACT_P) != 0, counter, st);
   return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -110,7 +114,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              float q_descale, float k_descale, float v_descale, void* stream) {
   if (B >= 1 && S >= 1 && B > INT64_MAX / S) return ATTN_ERR_SHAPE;
   return fwd(q, k, v, o, lse, nullptr, B >= 1 && S >= 1 ? B * S : 0, B, S, H, d_qk, d_v,
-             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, 0u, stream);
+             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, 0u, nullptr, stream);
 }
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -119,7 +123,18 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 void* stream) {
   if (B >= 1 && S >= 1 && B > INT64_MAX / S) return ATTN_ERR_SHAPE;
   return fwd(q, k, v, o, lse, nullptr, B >= 1 && S >= 1 ? B * S : 0, B, S, H, d_qk, d_v,
-             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, flags, stream);
+             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, flags, nullptr,
+             stream);
+}
+
+int attn_fwd_balanced(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale,
+                      int causal, int dtype, float q_descale, float k_descale, float v_descale,
+                      unsigned flags, int32_t* counter, void* stream) {
+  if (B >= 1 && S >= 1 && B > INT64_MAX / S) return ATTN_ERR_SHAPE;
+  return fwd(q, k, v, o, lse, nullptr, B >= 1 && S >= 1 ? B * S : 0, B, S, H, d_qk, d_v,
+             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, flags, counter,
+             stream);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -128,7 +143,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     float q_descale, float k_descale, float v_descale, void* stream) {
   if (!cu_seqlens) return ATTN_ERR_NULL;
   return fwd(q, k, v, o, lse, cu_seqlens, total, n_seqs, max_seqlen, H, d_qk, d_v,
-             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, 0u, stream);
+             softmax_scale, causal, dtype, q_descale, k_descale, v_descale, 0u, nullptr, stream);
 }
 
 int attn_amax_f32(const float* x, int64_t n, float* amax_out, void* stream) {

@@ -117,7 +117,7 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                      float* __restrict__ lse, const int32_t* __restrict__ cu, int64_t total,
                     int S_max, int H, int BH, int nqb, float c_log2,
-                     int causal) {
+                     int causal, int n_static, int q_cut, int* __restrict__ tail_ctr) {
   using LY = Layout<DQK, BN>;
   constexpr int kSteps = DQK / 16;                 // k-steps of the QK^T product
   constexpr int kNKB = BN / 32;                    // 32-key S blocks per tile
@@ -141,7 +141,9 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int half = lane >> 5;
 
   int qb, bh;
-  block_order(blockIdx.x, nqb, BH, qb, bh);
+  if (!block_claim(blockIdx.x, nqb, BH, n_static, q_cut, tail_ctr,
+                   reinterpret_cast<int*>(&sm.epi[0][0]), qb, bh))
+    return;
   const int b = bh / H;
   const int h = bh % H;
   // rows of this problem (a batch entry or a packed sequence); S is its length
@@ -537,19 +539,21 @@ attn_fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
 int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                      const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
-                     float softmax_scale, int causal, hipStream_t stream) {
+                     float softmax_scale, int causal, int32_t* tail_ctr, hipStream_t stream) {
   const int nqb = (S + kBM - 1) / kBM;
   const int BH = B * H;
-  const dim3 grid((unsigned)nqb * (unsigned)BH);
+  const BlockGrid bg = block_grid(nqb, BH, cu == nullptr, tail_ctr != nullptr);
+  if (bg.q_cut && launch_clear_i32(tail_ctr, stream) != 0) return -1;
+  const dim3 grid((unsigned)bg.grid);
   const float c_log2 = softmax_scale * 1.4426950408889634f;
   if (d_qk == 128)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 64>), grid, dim3(kThreads), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, cu, total, S,
-                       H, BH, nqb, c_log2, causal);
+                       H, BH, nqb, c_log2, causal, bg.n_static, bg.q_cut, (int*)tail_ctr);
   else
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<192, 32>), grid, dim3(kThreads), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, cu, total, S,
-                       H, BH, nqb, c_log2, causal);
+                       H, BH, nqb, c_log2, causal, bg.n_static, bg.q_cut, (int*)tail_ctr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

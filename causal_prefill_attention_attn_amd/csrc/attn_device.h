@@ -45,6 +45,39 @@ __device__ __forceinline__ void block_order(int id, int nqb, int BH, int& qb, in
   }
 }
 
+// The same order with the last part of the work shared among the XCDs.
+// Which XCD runs slowest changes from launch to launch, and a static split
+// leaves the others idle at the end (4-9% of the span at 32K tokens).  So the
+// q_cut shortest query blocks of every (b, h) leave the static lists: XCD
+// x = id & 7 runs blocks nqb-1 .. q_cut of its heads x, x+8, ... (ids below
+// n_static), and the workgroups after them claim the remaining blocks,
+// longest first, from a counter that starts at zero.  The fast XCDs reach
+// their claiming workgroups first and take more of them; workgroups that
+// find the pool empty end at once.  Outputs do not depend on which
+// workgroup computes a block.  lds_slot is a word of the workgroup's LDS not
+// yet in use.  Returns false when the workgroup has no block.
+__device__ __forceinline__ bool block_claim(int id, int nqb, int BH, int n_static, int q_cut,
+                                            int* ctr, int* lds_slot, int& qb, int& bh) {
+  if (q_cut == 0) {
+    block_order(id, nqb, BH, qb, bh);
+    return true;
+  }
+  if (id < n_static) {
+    const int x = id & 7, j = id >> 3, nl = nqb - q_cut;
+    qb = nqb - 1 - j % nl;
+    bh = x + 8 * (j / nl);
+    return true;
+  }
+  if (threadIdx.x == 0) *lds_slot = atomicAdd(ctr, 1);
+  __syncthreads();
+  const int t = __builtin_amdgcn_readfirstlane(*lds_slot);
+  __syncthreads();
+  if (t >= BH * q_cut) return false;
+  qb = q_cut - 1 - t / BH;
+  bh = t % BH;
+  return true;
+}
+
 // Rows of one attention problem -- one batch entry of a dense [B,S,H,D]
 // tensor, or one sequence of a packed [total,H,D] tensor -- and where its LSE
 // goes (dense [B,H,S], packed [H,total]).

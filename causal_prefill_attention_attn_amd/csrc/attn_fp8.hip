@@ -222,7 +222,8 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
                     const uint8_t* __restrict__ v, __bf16* __restrict__ o,
                     float* __restrict__ lse, const int32_t* __restrict__ cu, int64_t total,
                     int S_max, int H, int BH, int nqb, float c_log2, float c8n,
-                    float v_descale, int causal, int rot_o) {
+                    float v_descale, int causal, int rot_o, int n_static, int q_cut,
+                    int* __restrict__ tail_ctr) {
   using LY = Layout<DQK, BN>;
   constexpr int kWaves = 4 * kOcc;
   static_assert(kWaves <= 8, "one 4 KB output staging area per wave");
@@ -243,7 +244,9 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
   const int half = lane >> 5;
 
   int qb, bh;
-  block_order(blockIdx.x, nqb, BH, qb, bh);
+  if (!block_claim(blockIdx.x, nqb, BH, n_static, q_cut, tail_ctr,
+                   reinterpret_cast<int*>(&sm.epi[0][0]), qb, bh))
+    return;
   const int b = bh / H;
   const int h = bh % H;
   // rows of this problem (a batch entry or a packed sequence); S is its length
@@ -725,12 +728,15 @@ attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k
 int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
                     float softmax_scale, int causal, float q_descale, float k_descale,
-                    float v_descale, bool rot_o, bool exact_p, hipStream_t stream) {
+                    float v_descale, bool rot_o, bool exact_p, int32_t* tail_ctr,
+                    hipStream_t stream) {
   const int occ = 2;                      // waves per SIMD (register budget)
   const int bm = 128 * occ;               // query rows per workgroup
   const int nqb = (S + bm - 1) / bm;
   const int BH = B * H;
-  const dim3 grid((unsigned)nqb * (unsigned)BH);
+  const BlockGrid bg = block_grid(nqb, BH, cu == nullptr, tail_ctr != nullptr);
+  if (bg.q_cut && launch_clear_i32(tail_ctr, stream) != 0) return -1;
+  const dim3 grid((unsigned)bg.grid);
   const float c_log2 = softmax_scale * q_descale * k_descale * 1.4426950408889634f;
   // the lean code's scale 8 c in units of the 16-bit normalised conversion,
   // passed in so that its 32 FMAs per tile read it from a scalar register
@@ -740,7 +746,8 @@ int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float*
 #define CPATTN_LAUNCH_FP8(DQK, BN, LEAN, OCC)                                                     \
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, BN, LEAN, OCC>), grid, dim3(256 * OCC), 0, stream, \
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, cu, \
-                     total, S, H, BH, nqb, c_log2, c8n, v_descale, causal, (int)rot_o)
+                     total, S, H, BH, nqb, c_log2, c8n, v_descale, causal, (int)rot_o,       \
+                     bg.n_static, bg.q_cut, (int*)tail_ctr)
   if (d_qk == 128) {
     if (lean) CPATTN_LAUNCH_FP8(128, 64, true, 2);
     else CPATTN_LAUNCH_FP8(128, 64, false, 2);

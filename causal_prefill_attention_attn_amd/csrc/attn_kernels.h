@@ -10,10 +10,14 @@ namespace cpattn {
 // else B packed sequences of a [total,H,D] tensor bounded by cu[0..B]
 // (device), S being the longest.  Returns 0 or -1 (launch error).
 
+// tail_ctr: null, or a device word the launch may use to share the shortest
+// query blocks among the XCDs (block_claim); it is cleared by a kernel on the
+// same stream before the attention kernel.  Results do not depend on it.
+
 // BF16 q/k/v, d_qk in {128, 192}, d_v = 128.
 int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                      const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
-                     float softmax_scale, int causal, hipStream_t stream);
+                     float softmax_scale, int causal, int32_t* tail_ctr, hipStream_t stream);
 
 // FP8 E4M3FN q/k/v with per-tensor descales, d_qk in {128, 192}, d_v = 128;
 // rot_o: O rows times the normalised Hadamard matrix of order 128; exact_p:
@@ -21,7 +25,27 @@ int launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float
 int launch_attn_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int32_t* cu, int64_t total, int B, int S, int H, int d_qk,
                     float softmax_scale, int causal, float q_descale, float k_descale,
-                    float v_descale, bool rot_o, bool exact_p, hipStream_t stream);
+                    float v_descale, bool rot_o, bool exact_p, int32_t* tail_ctr,
+                    hipStream_t stream);
+
+// Grid of an attention launch with nqb query blocks per (b, h): the static
+// order, or, with a counter on the dense head-major path (at least 128
+// blocks per head, B*H a multiple of 8), the static part without the
+// nqb/4 shortest blocks of every head plus twice as many claiming
+// workgroups as there are claimed blocks.
+struct BlockGrid {
+  int grid, n_static, q_cut;
+};
+inline BlockGrid block_grid(int nqb, int BH, bool dense, bool counter) {
+  if (counter && dense && nqb >= 128 && (BH & 7) == 0) {
+    const int q_cut = nqb / 4;
+    const int n_static = BH * (nqb - q_cut);
+    return {n_static + 2 * BH * q_cut, n_static, q_cut};
+  }
+  return {nqb * BH, nqb * BH, 0};
+}
+// *p = 0, as a kernel on the stream (graph-capture safe)
+int launch_clear_i32(int32_t* p, hipStream_t stream);
 
 int launch_amax_f32(const float* x, int64_t n, float* amax_out, hipStream_t stream);
 int launch_quantize_e4m3(const float* x, int64_t n, float descale, uint8_t* out,

@@ -105,6 +105,11 @@ __global__ void descale_from_amax(float* p) {
 
 }  // namespace
 
+int launch_clear_i32(int32_t* p, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_u32, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(p));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_amax_f32(const float* x, int64_t n, float* amax_out, hipStream_t stream) {
   hipLaunchKernelGGL(zero_u32, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(amax_out));
   const int vec = aligned16(x) ? 1 : 0;

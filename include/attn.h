@@ -134,6 +134,35 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 void* stream);
 
 /*
+ * attn_fwd_balanced -- attn_fwd_ex whose last part of the work is shared
+ * among the chip's eight XCDs as they free up.  The operation is the one
+ * the pages state for the kernels (causal prefill attention over query and
+ * key blocks, "Como o motor de atencao FP8 da Zyphra funciona" on the
+ * miraibroadcast.com page); only the assignment of query blocks to
+ * workgroups differs.
+ *   counter  device, one int32 the call uses to hand out the shortest query
+ *            blocks (4-byte aligned, not overlapping q, k, v, o or lse); the
+ *            call clears it with a kernel on `stream` before the attention
+ *            kernel, so its contents on entry do not matter and no host-side
+ *            clear is needed (the pair can be captured in a HIP graph).
+ *            Calls that may run at the same time (on different streams)
+ *            must not share a counter.  NULL: same as attn_fwd_ex.
+ * Every other argument, check and return code is that of attn_fwd_ex.
+ * The counter is used when every (b, h) has at least 128 query blocks of
+ * 256 rows (S > 32512) and B*H is a multiple of 8; the q_cut = nqb/4
+ * shortest blocks of every head are then claimed, longest first, through
+ * one atomic add per claiming workgroup, by workgroups placed after the
+ * fixed part of the grid, so the XCDs that finish their fixed part first
+ * take more of them.  Otherwise the counter is left alone.
+ * Results equal those of attn_fwd_ex with the same flags bit for bit: each
+ * block is computed the same way whichever workgroup runs it.
+ */
+int attn_fwd_balanced(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t S, int64_t H, int d_qk, int d_v, float softmax_scale,
+                      int causal, int dtype, float q_descale, float k_descale, float v_descale,
+                      unsigned flags, int32_t* counter, void* stream);
+
+/*
  * attn_fwd_varlen -- attn_fwd over a batch of sequences of different
  * lengths packed along the token dimension, each attending only within
  * itself (variable-length batches, which "Ce que couvrent les noyaux" on the

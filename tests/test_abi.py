@@ -33,7 +33,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["attn_version", "attn_status_string", "attn_fwd", "attn_fwd_ex",
-                            "attn_fwd_varlen",
+                            "attn_fwd_balanced", "attn_fwd_varlen",
                             "attn_amax_f32", "attn_quantize_fp8",
                             "attn_quantize_e4m3", "attn_hadamard_f32", "attn_hadamard_bf16",
                             "attn_hadamard_amax_f32", "attn_hadamard_quantize_e4m3",
@@ -83,6 +83,26 @@ def _call(**over):
 ])
 def test_attn_fwd_rejects(lib, over, code):
     assert _call(**over) == code
+
+
+def test_balanced_entry_point_checks_its_counter(lib):
+    """attn_fwd_balanced runs attn_fwd's checks, plus: the counter (when
+    given) must be 4-byte aligned and must not overlap any tensor.  Only
+    rejected calls are made here (no GPU)."""
+    C = 0x70000000
+
+    def call(counter, **over):
+        a = dict(GOOD)
+        a.update(over)
+        return pkg.attn_fwd_balanced(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["S"],
+                                     a["H"], a["d_qk"], a["d_v"], a["softmax_scale"],
+                                     a["causal"], a["dtype"], a["q_descale"], a["k_descale"],
+                                     a["v_descale"], 0, counter, a["stream"])
+    assert call(C + 2) == -6
+    assert call(O) == -7 and call(Q + 64) == -7 and call(L) == -7 and call(V + 4) == -7
+    assert call(C, q=None) == -1 and call(C, S=0) == -2 and call(C, dtype=2) == -3
+    assert call(C, d_qk=64) == -4 and call(C, softmax_scale=0.0) == -5
+    assert call(None, o=O + 2) == -6
 
 
 def test_bf16_ignores_descales_fp8_checks_them(lib):
