@@ -48,10 +48,11 @@ __device__ __forceinline__ void block_order(int id, int nqb, int BH, int& qb, in
 // The same order with the last part of the work shared among the XCDs.
 // Which XCD runs slowest changes from launch to launch, and a static split
 // leaves the others idle at the end (4-9% of the span at 32K tokens).  So the
-// q_cut shortest query blocks of every (b, h) leave the static lists: XCD
-// x = id & 7 runs blocks nqb-1 .. q_cut of its heads x, x+8, ... (ids below
-// n_static), and the workgroups after them claim the remaining blocks,
-// longest first, from a counter that starts at zero.  The fast XCDs reach
+// q_cut shortest query blocks of every (b, h) leave the static lists: in the
+// head-major order XCD x = id & 7 runs blocks nqb-1 .. q_cut of its heads
+// x, x+8, ...; in the query-block-major order the first n_static ids are
+// those blocks already.  The workgroups after the static ids claim the
+// remaining blocks, longest first, from a counter that starts at zero.  The fast XCDs reach
 // their claiming workgroups first and take more of them; workgroups that
 // find the pool empty end at once.  Outputs do not depend on which
 // workgroup computes a block.  lds_slot is a word of the workgroup's LDS not
@@ -63,9 +64,13 @@ __device__ __forceinline__ bool block_claim(int id, int nqb, int BH, int n_stati
     return true;
   }
   if (id < n_static) {
-    const int x = id & 7, j = id >> 3, nl = nqb - q_cut;
-    qb = nqb - 1 - j % nl;
-    bh = x + 8 * (j / nl);
+    if (nqb >= 128 && (BH & 7) == 0) {
+      const int x = id & 7, j = id >> 3, nl = nqb - q_cut;
+      qb = nqb - 1 - j % nl;
+      bh = x + 8 * (j / nl);
+    } else {
+      block_order(id, nqb, BH, qb, bh);  // its first n_static ids: blocks nqb-1 .. q_cut
+    }
     return true;
   }
   if (threadIdx.x == 0) *lds_slot = atomicAdd(ctr, 1);

@@ -148,12 +148,12 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  *            Calls that may run at the same time (on different streams)
  *            must not share a counter.  NULL: same as attn_fwd_ex.
  * Every other argument, check and return code is that of attn_fwd_ex.
- * The counter is used when every (b, h) has at least 128 query blocks of
- * 256 rows (S > 32512) and B*H is a multiple of 8; the q_cut = nqb/4
- * shortest blocks of every head are then claimed, longest first, through
- * one atomic add per claiming workgroup, by workgroups placed after the
- * fixed part of the grid, so the XCDs that finish their fixed part first
- * take more of them.  Otherwise the counter is left alone.
+ * The counter is used when every (b, h) has at least 32 query blocks of
+ * 256 rows (S > 7936); the q_cut = nqb/4 shortest blocks of every head are
+ * then claimed, longest first, through one atomic add per claiming
+ * workgroup, by workgroups placed after the fixed part of the grid, so the
+ * XCDs that finish their fixed part first take more of them.  Otherwise the
+ * counter is left alone.
  * Results equal those of attn_fwd_ex with the same flags bit for bit: each
  * block is computed the same way whichever workgroup runs it.
  */

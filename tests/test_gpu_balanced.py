@@ -1,10 +1,12 @@
 """attn_fwd_balanced: the shortest query blocks handed out through a counter
 give the same bits as attn_fwd_ex's fixed order.
 
-Shapes with at least 128 query blocks of 256 rows per head and B*H a
-multiple of 8 take the shared tail (q_cut = nqb/4 blocks of every head,
-claimed by 2*B*H*q_cut workgroups, each adding one to the counter, so the
-counter ends at that number). Other shapes leave the counter alone. The
+Shapes with at least 32 query blocks of 256 rows per head take the shared
+tail: q_cut = nqb/4 blocks of every head, claimed by 2*B*H*q_cut workgroups.
+Each claiming workgroup adds one to the counter, so the counter ends at that
+number. At 128 blocks or more with B*H a multiple of 8, the fixed part is
+in the head-major order per XCD; otherwise it is in the query-block-major
+order. Shorter problems leave the counter alone. The
 counter's contents on entry do not matter: the call clears it first. The
 parity of these outputs with the oracle is the subject of the full-size
 tests, which call through flash_attn_func and so through this entry point.
@@ -57,6 +59,10 @@ def _same(a, b):
     (2, 32768 + 100, 4, 192, FP8, 0),    # 129 blocks per head, ragged last block
     (1, 32768, 8, 128, BF16, 0),
     (1, 32768, 8, 192, BF16, 0),
+    (1, 32768, 4, 128, FP8, 0),          # B*H = 4: query-block-major order
+    (3, 33000, 3, 128, FP8, 0),          # B*H = 9, ragged
+    (1, 16384, 32, 128, FP8, 0),         # 64 blocks per head
+    (2, 8192, 4, 192, BF16, 0),          # 32 blocks per head, the smallest shared case
 ])
 def test_shared_tail_gives_the_fixed_order_bits(B, S, H, dqk, dtype, flags):
     q, k, v = _inputs(B, S, H, dqk, dtype, seed=S + H + dqk + flags)
@@ -74,10 +80,10 @@ def test_shared_tail_gives_the_fixed_order_bits(B, S, H, dqk, dtype, flags):
     assert _same(got, ref)
 
 
-@pytest.mark.parametrize("B,S,H", [(1, 4096, 8), (1, 32768, 4), (3, 33000, 3)])
+@pytest.mark.parametrize("B,S,H", [(1, 4096, 8), (2, 7936, 4), (1, 300, 3)])
 def test_other_shapes_leave_the_counter_alone(B, S, H):
-    """Fewer than 128 blocks per head, or B*H not a multiple of 8: the fixed
-    order, the counter untouched."""
+    """Fewer than 32 blocks per head: the fixed order, the counter
+    untouched."""
     q, k, v = _inputs(B, S, H, 128, FP8, seed=7 * S + H)
     ref = _run("ex", q, k, v, B, S, H, 128, FP8, 0)
     counter = torch.full((1,), 777, dtype=torch.int32, device=DEV)
