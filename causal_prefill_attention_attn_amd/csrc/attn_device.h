@@ -52,11 +52,12 @@ __device__ __forceinline__ void block_order(int id, int nqb, int BH, int& qb, in
 // head-major order XCD x = id & 7 runs blocks nqb-1 .. q_cut of its heads
 // x, x+8, ...; in the query-block-major order the first n_static ids are
 // those blocks already.  The workgroups after the static ids claim the
-// remaining blocks, longest first, from a counter that starts at zero.  The fast XCDs reach
-// their claiming workgroups first and take more of them; workgroups that
-// find the pool empty end at once.  Outputs do not depend on which
-// workgroup computes a block.  lds_slot is a word of the workgroup's LDS not
-// yet in use.  Returns false when the workgroup has no block.
+// remaining blocks, longest first, from a counter that starts at zero.  The
+// fast XCDs reach their claiming workgroups first and take more of them;
+// workgroups that find the pool empty end at once.  Outputs do not depend
+// on which workgroup computes a block.  lds_slot is a word of the
+// workgroup's LDS not yet in use.  Returns false when the workgroup has no
+// block.
 __device__ __forceinline__ bool block_claim(int id, int nqb, int BH, int n_static, int q_cut,
                                             int* ctr, int* lds_slot, int& qb, int& bh) {
   if (q_cut == 0) {
