@@ -100,3 +100,33 @@ def test_flash_attn_func_balanced_and_fixed_agree():
     b = pkg.flash_attn_func(q, k, v, balanced=False)
     torch.cuda.synchronize()
     assert _same(a, b)
+
+
+def test_shared_tail_replays_in_a_graph():
+    """The counter clear is a kernel, so a captured flash_attn_func on the
+    shared-tail path replays correctly. At 8192 tokens (32 blocks per head)
+    each replay must claim its blocks again, and every output is poisoned
+    before the replay."""
+    q, k, v = (x.view(torch.float8_e4m3fn) for x in _inputs(1, 8192, 2, 128, FP8, seed=21))
+    o = torch.empty((1, 8192, 2, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((1, 2, 8192), dtype=torch.float32, device=DEV)
+    ref = pkg.flash_attn_func(q, k, v, balanced=False)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pkg.flash_attn_func(q, k, v, out=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same((o, lse), ref), rep
+        pkg.flash_attn_func(k, q, v)  # unrelated eager work between replays
+        torch.cuda.synchronize()
